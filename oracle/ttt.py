@@ -1,0 +1,294 @@
+"""Plain CPU reference of the VGG-T^3 TTT layer (test infrastructure only).
+
+Sources (web pages on VGG-T^3; cited by title and section):
+  [BLOG]  neteralex.cn blog post "VGG-T^3 3D reconstruction at scale" — sections on
+          writing the scene into an MLP by test-time training (the argmin objective
+          and the read o_i = T_theta*(q_i)), on why a plain K->V map is degenerate
+          (ShortConv2D on V), and on linear scaling (gradient split over minibatches).
+  [GRAPH] paper-graph summary "VGG-T3: Offline Feed-Forward 3D Reconstruction at
+          Scale" — section 3.4: "The Test-Time Training (TTT) Framework" (Eq. 3
+          optimisation, Eq. 4 query), "Non-Linear Spatial Mixing via ShortConv2D"
+          (reshape / 3x3 conv / flatten) with its Appendix A note that camera and
+          register tokens skip the conv, "TTT MLP Architecture" (SwiGLU), and
+          "Large-Scale Inference Strategies" (Eq. 5 minibatch gradient sum, query mode).
+
+Readings taken where the pages are open (each is listed in the design notes):
+  * inner loss: per-token mean squared error over the d outputs, summed over all
+    tokens, L_h = sum_i (1/d)||T(k_i) - v'_i||^2, heads independent;
+  * optimiser: plain full-batch gradient descent, all three matrices updated
+    together from the gradient at the current theta; one step = one full pass;
+  * T(x) = (silu(x W_g) * (x W_u)) W_d, no biases, Swish with beta = 1;
+  * ShortConv2D: depthwise 3x3 cross-correlation, stride 1, zero padding,
+    no bias, one filter per channel, within one view; special tokens copied.
+
+Everything here is float64 except ``shortconv``, whose result is defined bit for
+bit by a float32 evaluation order (the "conv contract").
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# Rounding helpers
+# ----------------------------------------------------------------------------
+
+
+def bf16_round(x) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even), as float32.
+
+    bfloat16 keeps the top 16 bits of an IEEE binary32; rounding adds half an
+    ulp of the kept part (0x7FFF plus the kept part's lowest bit, which breaks
+    ties towards even) before truncating. NaNs stay NaN.
+    """
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = x.view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)) & np.uint64(0xFFFF)
+    out = (r << np.uint64(16)).astype(np.uint32).view(np.float32).copy()
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = np.float32(np.nan)
+    return out.reshape(x.shape)
+
+
+# ----------------------------------------------------------------------------
+# ShortConv2D  ([GRAPH] "Non-Linear Spatial Mixing via ShortConv2D"; [BLOG]
+# section on the degenerate K->V map)
+# ----------------------------------------------------------------------------
+
+
+def _check_layout(n: int, n_views: int, grid_h: int, grid_w: int, n_special: int) -> int:
+    tpv = n_special + grid_h * grid_w
+    if n != n_views * tpv:
+        raise ValueError(f"{n} tokens do not match {n_views} views x {tpv} tokens")
+    return tpv
+
+
+def shortconv(V, w, n_views: int, grid_h: int, grid_w: int, n_special: int,
+              out: str = "bf16") -> np.ndarray:
+    """V' = ShortConv2D(V) under the float32 conv contract.
+
+    Each view's patch tokens are reshaped to a (grid_h, grid_w, C) grid, every
+    channel c is cross-correlated with its own 3x3 filter w[c] (zero padding,
+    same size) and the grid is flattened back; the view's special tokens are
+    copied unchanged.
+
+    Contract (fixes the result bit for bit): per output element the nine taps
+    are visited with the row offset outermost and the column offset innermost,
+    both from -1 to +1; starting from acc = +0.0f, each tap does
+    acc = fl32(acc + fl32(w * v)) — a separately rounded float32 product and
+    sum, never a fused multiply-add; taps outside the grid see v = 0. With
+    ``out="bf16"`` the float32 result is rounded to bfloat16 (ties to even).
+
+    Args: V [n, C] (float32 or exactly-widened bf16 values), w [C, 3, 3] float32.
+    Returns float32 [n, C] (bf16-representable values when out == "bf16").
+    """
+    V32 = np.asarray(V, dtype=np.float32)
+    w32 = np.asarray(w, dtype=np.float32)
+    n, C = V32.shape
+    tpv = _check_layout(n, n_views, grid_h, grid_w, n_special)
+    res = V32.copy()  # special tokens pass through untouched
+    grid = V32.reshape(n_views, tpv, C)[:, n_special:, :].reshape(n_views, grid_h, grid_w, C)
+    padded = np.zeros((n_views, grid_h + 2, grid_w + 2, C), dtype=np.float32)
+    padded[:, 1:-1, 1:-1, :] = grid
+    acc = np.zeros((n_views, grid_h, grid_w, C), dtype=np.float32)
+    for dy in (-1, 0, 1):
+        for dx in (-1, 0, 1):
+            tap = padded[:, 1 + dy:1 + dy + grid_h, 1 + dx:1 + dx + grid_w, :]
+            prod = (w32[:, dy + 1, dx + 1] * tap).astype(np.float32)  # fl32(w * v)
+            acc = (acc + prod).astype(np.float32)  # fl32(acc + p)
+    if out == "bf16":
+        acc = bf16_round(acc)
+    elif out != "f32":
+        raise ValueError(out)
+    res.reshape(n_views, tpv, C)[:, n_special:, :] = acc.reshape(n_views, grid_h * grid_w, C)
+    return res
+
+
+def shortconv_direct(V, w, n_views: int, grid_h: int, grid_w: int, n_special: int) -> np.ndarray:
+    """Brute-force depthwise 3x3 convolution in float64 with explicit loops.
+
+    Written straight from the definition V'[y, x, c] = sum_{a,b in {-1,0,1}}
+    w[c, a+1, b+1] * V[y+a, x+b, c] over taps inside the grid. Pure Python: tiny
+    inputs only. Used to pin ``shortconv``.
+    """
+    V64 = np.asarray(V, dtype=np.float64)
+    w64 = np.asarray(w, dtype=np.float64)
+    n, C = V64.shape
+    tpv = _check_layout(n, n_views, grid_h, grid_w, n_special)
+    res = V64.copy()
+    for v in range(n_views):
+        base = v * tpv + n_special
+        for y in range(grid_h):
+            for x in range(grid_w):
+                for c in range(C):
+                    s = 0.0
+                    for a in (-1, 0, 1):
+                        for b in (-1, 0, 1):
+                            yy, xx = y + a, x + b
+                            if 0 <= yy < grid_h and 0 <= xx < grid_w:
+                                s += w64[c, a + 1, b + 1] * V64[base + yy * grid_w + xx, c]
+                    res[base + y * grid_w + x, c] = s
+    return res
+
+
+# ----------------------------------------------------------------------------
+# Fast-weight SwiGLU MLP  ([GRAPH] "TTT MLP Architecture and Inner Optimization")
+# ----------------------------------------------------------------------------
+
+
+def split_theta(theta_h, d: int, m: int):
+    """One head's flat parameters -> (W_g [d,m], W_u [d,m], W_d [m,d]), float64."""
+    t = np.asarray(theta_h, dtype=np.float64).reshape(-1)
+    if t.size != 3 * d * m:
+        raise ValueError("theta size")
+    return (t[:d * m].reshape(d, m), t[d * m:2 * d * m].reshape(d, m),
+            t[2 * d * m:].reshape(m, d))
+
+
+def join_theta(Wg, Wu, Wd) -> np.ndarray:
+    return np.concatenate([np.ravel(Wg), np.ravel(Wu), np.ravel(Wd)])
+
+
+def _sigmoid(x):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def swiglu_forward(X, Wg, Wu, Wd, act: str = "silu") -> dict:
+    """T(X) = (act(X W_g) * (X W_u)) W_d with intermediates.
+
+    act = "silu" is the SwiGLU gate silu(g) = g * sigmoid(g). act = "one" makes
+    the gate the constant 1 (T(X) = X W_u W_d); it exists only so that tests can
+    pin the backward pass against closed forms.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    G = X @ Wg
+    U = X @ Wu
+    if act == "silu":
+        S = _sigmoid(G)
+        A = G * S
+    elif act == "one":
+        S = None
+        A = np.ones_like(G)
+    else:
+        raise ValueError(act)
+    H = A * U
+    Y = H @ Wd
+    return {"G": G, "U": U, "S": S, "A": A, "H": H, "Y": Y}
+
+
+def head_grad(K, Vp, Wg, Wu, Wd, act: str = "silu", chunk: int = 32768):
+    """Loss and gradient of one head's inner objective at (W_g, W_u, W_d).
+
+    L = sum_i (1/d) ||T(k_i) - v'_i||^2 (Eq. 3 of [GRAPH] with a squared-error
+    L_t). The gradient is accumulated over fixed token chunks, which Eq. 5 of
+    [GRAPH] ("Minibatch gradient decomposition") makes exact. Backward pass by
+    the chain rule through T:
+        R = Y - V', dY = (2/d) R, g_Wd = H^T dY, dH = dY W_d^T,
+        dU = dH * act(G), dG = dH * U * act'(G), g_Wg = K^T dG, g_Wu = K^T dU,
+    with silu'(g) = s (1 + g (1 - s)), s = sigmoid(g).
+    Returns (loss, g_Wg, g_Wu, g_Wd), all float64.
+    """
+    K = np.asarray(K)
+    Vp = np.asarray(Vp)
+    n, d = K.shape
+    loss = 0.0
+    gWg = np.zeros_like(Wg)
+    gWu = np.zeros_like(Wu)
+    gWd = np.zeros_like(Wd)
+    for s in range(0, n, chunk):
+        k = np.asarray(K[s:s + chunk], dtype=np.float64)
+        v = np.asarray(Vp[s:s + chunk], dtype=np.float64)
+        f = swiglu_forward(k, Wg, Wu, Wd, act)
+        R = f["Y"] - v
+        loss += float(np.sum(R * R)) / d
+        dY = (2.0 / d) * R
+        gWd += f["H"].T @ dY
+        dH = dY @ Wd.T
+        dU = dH * f["A"]
+        if act == "silu":
+            S = f["S"]
+            dG = dH * f["U"] * (S * (1.0 + f["G"] * (1.0 - S)))
+        else:
+            dG = np.zeros_like(dH)
+        gWg += k.T @ dG
+        gWu += k.T @ dU
+    return loss, gWg, gWu, gWd
+
+
+def _head_cols(h: int, d: int) -> slice:
+    return slice(h * d, (h + 1) * d)
+
+
+def ttt_grad(K, Vp, theta, n_heads: int, d: int, m: int, act: str = "silu",
+             chunk: int = 32768):
+    """Gradient of every head's inner loss at theta: (grad [H, 3dm], loss [H])."""
+    theta = np.asarray(theta, dtype=np.float64).reshape(n_heads, 3 * d * m)
+    grad = np.zeros_like(theta)
+    loss = np.zeros(n_heads)
+    for h in range(n_heads):
+        Wg, Wu, Wd = split_theta(theta[h], d, m)
+        cols = _head_cols(h, d)
+        L, gg, gu, gd = head_grad(K[:, cols], Vp[:, cols], Wg, Wu, Wd, act, chunk)
+        grad[h] = join_theta(gg, gu, gd)
+        loss[h] = L
+    return grad, loss
+
+
+def ttt_loss(K, Vp, theta, n_heads: int, d: int, m: int, act: str = "silu") -> np.ndarray:
+    """Per-head inner loss sum_i (1/d)||T(k_i) - v'_i||^2 at theta (no gradient)."""
+    theta = np.asarray(theta, dtype=np.float64).reshape(n_heads, 3 * d * m)
+    out = np.zeros(n_heads)
+    for h in range(n_heads):
+        Wg, Wu, Wd = split_theta(theta[h], d, m)
+        cols = _head_cols(h, d)
+        f = swiglu_forward(np.asarray(K[:, cols], dtype=np.float64), Wg, Wu, Wd, act)
+        R = f["Y"] - np.asarray(Vp[:, cols], dtype=np.float64)
+        out[h] = float(np.sum(R * R)) / d
+    return out
+
+
+def ttt_apply(theta, grad, lr: float) -> np.ndarray:
+    """One plain gradient-descent update theta - lr * grad (all matrices at once)."""
+    return np.asarray(theta, dtype=np.float64) - lr * np.asarray(grad, dtype=np.float64)
+
+
+def ttt_write(K, Vp, theta0, n_heads: int, d: int, m: int, lr: float, steps: int,
+              act: str = "silu", reduction: str = "sum", chunk: int = 32768):
+    """Fit the fast weights: `steps` full-batch gradient-descent steps from theta0.
+
+    Eq. 3 of [GRAPH] approximated by a fixed number of plain GD steps; each step
+    is one pass over all n tokens at the current theta followed by one update
+    with the accumulated gradient ([GRAPH] "Large-Scale Inference Strategies":
+    accumulate over minibatches, then apply). ``reduction="mean"`` divides loss
+    and gradient by n (an alternative reading kept for tests only).
+    Returns (theta* [H, 3dm], losses [steps, H] at the theta each step starts
+    from, grads [steps, H, 3dm]).
+    """
+    theta = np.asarray(theta0, dtype=np.float64).reshape(n_heads, 3 * d * m).copy()
+    n = np.asarray(K).shape[0]
+    losses = np.zeros((steps, n_heads))
+    grads = np.zeros((steps, n_heads, 3 * d * m))
+    for s in range(steps):
+        g, L = ttt_grad(K, Vp, theta, n_heads, d, m, act, chunk)
+        if reduction == "mean":
+            g, L = g / n, L / n
+        elif reduction != "sum":
+            raise ValueError(reduction)
+        losses[s] = L
+        grads[s] = g
+        theta = ttt_apply(theta, g, lr)
+    return theta, losses, grads
+
+
+def ttt_read(Q, theta, n_heads: int, d: int, m: int, act: str = "silu") -> np.ndarray:
+    """Read pass o_i = T_theta(q_i) per head (Eq. 4 of [GRAPH]); float64 [n, C]."""
+    Q = np.asarray(Q)
+    theta = np.asarray(theta, dtype=np.float64).reshape(n_heads, 3 * d * m)
+    O = np.zeros((Q.shape[0], n_heads * d))
+    for h in range(n_heads):
+        Wg, Wu, Wd = split_theta(theta[h], d, m)
+        cols = _head_cols(h, d)
+        O[:, cols] = swiglu_forward(np.asarray(Q[:, cols], dtype=np.float64), Wg, Wu, Wd, act)["Y"]
+    return O
