@@ -1,0 +1,241 @@
+"""Benchmark of the VGG-T^3 TTT layer on one MI355X.
+
+One step = one pass of the whole layer over the scene, inputs resident in HBM:
+  theta <- theta0; V' = ShortConv2D(V); `steps` x (gradient partials over all
+  tokens -> fixed-tree reduce + theta -= lr*g); O = read(Q).
+This is exactly the kernel sequence vggt3_ttt_write runs (the write's two
+halves are called through the split C ABI so that the gradient kernel can be
+bracketed by HIP events on the stream it runs on).
+
+Prints ONE JSON line (rank 0) with tokens/s over the scene, the roofline of the
+dominant kernel (the bf16-MFMA gradient pass), per-phase times, and the CPU
+oracle's throughput on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--config views1000]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "TTT-layer tokens/sec (write+read) at 1000 views; % bf16 MFMA peak"
+GRAD_KERNEL = "grad_partial_bf16_kernel"
+GRAD_SOURCE = os.path.join(ROOT, "test_layer_amd", "csrc", "ttt_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grad_partial_bf16_views1000_traffic.json")
+
+
+def flops_per_token(cfg):
+    """Algorithmic flops per token: write step = 7 GEMM passes of 2*d*m per head
+    (G, U, Y forward; dH backward; three weight gradients); read = 3."""
+    per_gemm = 2 * cfg.d_head * cfg.d_hidden * cfg.n_heads
+    return 7 * per_gemm, 3 * per_gemm
+
+
+def source_sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per launch of the gradient kernel from the committed rocprofv3
+    counter summary, or None if absent or taken on different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_sha256(GRAD_SOURCE):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(inp, cfg, target_s=15.0, max_views=64):
+    """The fp64 CPU oracle, as it stands, on the first s views of the same
+    scene (conv, `steps` write steps over those tokens, read). s doubles from
+    2 views until one run takes >= target_s / 2 (or max_views)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 0) for i in info if i.get("user_api") == "blas"] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    tpv = cfg.tokens_per_view
+    w = inp.conv_w.cpu().numpy()
+    th0 = inp.theta0.cpu().numpy()
+    views = 2
+    while True:
+        n = views * tpv
+        K = inp.K[:n].to(torch.float32).cpu().numpy().astype(np.float64)
+        V = inp.V[:n].to(torch.float32).cpu().numpy()
+        Q = inp.Q[:n].to(torch.float32).cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        Vp = oracle.shortconv(V, w, views, cfg.grid_h, cfg.grid_w, cfg.n_special, out="bf16")
+        th, _, _ = oracle.ttt_write(K, Vp.astype(np.float64), th0, cfg.n_heads, cfg.d_head, cfg.d_hidden,
+                                    cfg.lr, cfg.steps)
+        oracle.ttt_read(Q, th, cfg.n_heads, cfg.d_head, cfg.d_hidden)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 2 or views >= max_views or views * 2 > cfg.n_views:
+            break
+        views *= 2
+    return {
+        "value": n / dt,
+        "unit": "tokens/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"first {views} views ({n} tokens) of the same scene: fp64 numpy oracle conv + "
+                   f"{cfg.steps} write steps + read over those tokens, all {cfg.n_heads} heads; {dt:.2f} s; "
+                   f"host {platform.processor() or platform.machine()}, {os.cpu_count()} logical CPUs"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="views1000")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run one plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; multi-GPU runs (--gpus > 1) are not "
+              "supported (the layer's data-parallel sharding is described in DESIGN.md only).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import test_layer_amd as tla
+    from synth import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(cfg, dev)
+    n, H, d, m = cfg.n_tokens, cfg.n_heads, cfg.d_head, cfg.d_hidden
+    dt_code = tla.BF16 if cfg.dtype == "bf16" else tla.F32
+    Vp = torch.empty_like(inp.V)
+    O = torch.empty_like(inp.Q)
+    theta = inp.theta0.clone()
+    ws = tla.make_workspace(n, H, d, m, dt_code, dev)
+    loss = torch.zeros((cfg.steps, H), device=dev)
+    nq = inp.Q.shape[0]
+
+    def step(ev=None):
+        theta.copy_(inp.theta0)
+        if ev:
+            ev["c0"].record()
+        tla.shortconv(inp.V, inp.conv_w, cfg.n_views, cfg.grid_h, cfg.grid_w, cfg.n_special, out=Vp)
+        if ev:
+            ev["c1"].record()
+        for s in range(cfg.steps):
+            if ev:
+                ev["g"][s][0].record()
+            tla.ttt_grad_partials(inp.K, Vp, theta, H, ws)
+            if ev:
+                ev["g"][s][1].record()
+            tla.ttt_reduce(ws, n, H, d, m, dt_code, tla.REDUCE_APPLY, theta, cfg.lr, loss[s])
+        if ev:
+            ev["w1"].record()
+        tla.ttt_read(inp.Q, theta, H, out=O)
+        if ev:
+            ev["r1"].record()
+
+    def mk():
+        return torch.cuda.Event(enable_timing=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [{"c0": mk(), "c1": mk(), "w1": mk(), "r1": mk(),
+               "g": [(mk(), mk()) for _ in range(cfg.steps)]} for _ in range(args.steps)]
+    start, end = mk(), mk()
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(events[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+
+    conv_ms = sum(e["c0"].elapsed_time(e["c1"]) for e in events) / args.steps
+    write_ms = sum(e["c1"].elapsed_time(e["w1"]) for e in events) / args.steps
+    read_ms = sum(e["w1"].elapsed_time(e["r1"]) for e in events) / args.steps
+    grad_ms = [a.elapsed_time(b) for e in events for (a, b) in e["g"]]
+    grad_avg_ms = sum(grad_ms) / len(grad_ms)
+
+    fw, fr = flops_per_token(cfg)
+    grad_flops = fw * n  # per launch of the gradient kernel
+    achieved = grad_flops / (grad_avg_ms * 1e-3) / 1e12
+    mlp_frac = (fw * n * cfg.steps + fr * nq) / ((write_ms + read_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+    esz = 2 if cfg.dtype == "bf16" else 4
+    conv_bytes = 2 * n * H * d * esz
+    read_bytes = 2 * nq * H * d * esz
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": METRIC,
+        "value": n / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.description}",
+            "n_views": cfg.n_views, "tokens_per_view": cfg.tokens_per_view, "n_tokens": n,
+            "n_heads": H, "d_head": d, "d_hidden": m, "write_steps": cfg.steps, "lr": cfg.lr,
+            "read_tokens": nq, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": GRAD_KERNEL,
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": load_traffic(),
+            "avg_launch_ms": grad_avg_ms,
+            "flops_per_launch": grad_flops,
+        },
+        "phases_ms": {"conv": conv_ms, "write": write_ms, "read": read_ms},
+        "mfma_frac_mlp_contractions": mlp_frac,
+        "hbm_GBps": {"conv": conv_bytes / (conv_ms * 1e-3) / 1e9, "read": read_bytes / (read_ms * 1e-3) / 1e9},
+        "final_loss_head0": float(loss[-1, 0].item()),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, cfg)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

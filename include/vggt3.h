@@ -1,0 +1,200 @@
+/*
+ * vggt3.h — C ABI of the MI355X (gfx950) VGG-T^3 test-time-training layer.
+ *
+ * The layer replaces a global softmax-attention layer by a fast-weight SwiGLU
+ * MLP that is fitted to the scene at inference time and then queried:
+ *
+ *   1. ShortConv2D  V -> V'   (depthwise 3x3 over each view's patch grid)
+ *   2. write        theta* = a few gradient-descent steps on
+ *                   sum_i (1/d)||T_theta(k_i) - v'_i||^2          (per head)
+ *   3. read         o_i = T_theta*(q_i)
+ *
+ * with T(x) = (silu(x W_g) * (x W_u)) W_d per head (no biases).
+ *
+ * Sources, cited by page title and section:
+ *   [GRAPH] paper-graph summary "VGG-T3: Offline Feed-Forward 3D Reconstruction
+ *           at Scale", section 3.4: "The Test-Time Training (TTT) Framework"
+ *           (Eq. 3 optimisation, Eq. 4 query), "Non-Linear Spatial Mixing via
+ *           ShortConv2D" (+ Appendix A: special tokens skip the conv), "TTT MLP
+ *           Architecture and Inner Optimization" (SwiGLU fast weights),
+ *           "Large-Scale Inference Strategies" (Eq. 5 minibatch gradient sum,
+ *           query mode).
+ *   [BLOG]  neteralex.cn "VGG-T^3 3D reconstruction at scale": the Update-then-
+ *           Apply use of the layer, the per-minibatch gradient split, query mode
+ *           with frozen weights, and the released interface's default of 1 step.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *     aligned. The library allocates no device memory and keeps no state
+ *     between calls apart from a per-thread last-error string.
+ *   - Token tensors (K, V, V', Q, O) are row-major [n_tokens][C] with
+ *     C = n_heads * d_head; head h owns columns h*d_head .. h*d_head+d_head-1.
+ *     Within a scene, tokens are grouped by view, and each view is
+ *     [n_special special tokens][grid_h*grid_w patch tokens, row-major].
+ *   - dtype VGGT3_BF16: token tensors are bfloat16, MLP contractions run on
+ *     bf16 MFMA with fp32 accumulation. dtype VGGT3_F32: token tensors are
+ *     float32 and all arithmetic is fp32.
+ *   - Fast weights theta are float32 [n_heads][3*d_head*d_hidden]; per head the
+ *     three row-major blocks W_g [d_head][d_hidden], W_u [d_head][d_hidden],
+ *     W_d [d_hidden][d_head].
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is enqueued and a negative vggt3_status is returned. Work
+ *     is asynchronous on `stream` (a hipStream_t; NULL = default stream);
+ *     device faults surface at the caller's next synchronisation.
+ *   - Results are deterministic: identical inputs on the same GPU give
+ *     bitwise-identical outputs (no atomics; fixed reduction trees).
+ *   - Calls that share a workspace must not run concurrently.
+ */
+#ifndef VGGT3_H
+#define VGGT3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  VGGT3_OK = 0,
+  VGGT3_EINVAL = -1,       /* null/misaligned/aliased pointer, negative size, bad lr/steps */
+  VGGT3_EUNSUPPORTED = -2, /* shape or dtype this build has no kernel for */
+  VGGT3_EWORKSPACE = -3,   /* workspace missing or smaller than vggt3_ttt_workspace_bytes */
+  VGGT3_EHIP = -4          /* the HIP runtime refused a launch */
+};
+
+enum { VGGT3_BF16 = 0, VGGT3_F32 = 1 };
+
+/* Library version (major*10000 + minor*100 + patch). */
+int vggt3_version(void);
+
+/* Text for a status code; never NULL. */
+const char* vggt3_status_str(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* vggt3_last_error(void);
+
+/*
+ * ShortConv2D: V' = depthwise 3x3 convolution of each view's patch grid
+ * ([GRAPH] "Non-Linear Spatial Mixing via ShortConv2D": reshape the value
+ * tokens to (views, H/p, W/p, C), apply one 3x3 filter per channel, flatten
+ * back; Appendix A: camera/register tokens are passed through unchanged).
+ *
+ *   V        [n_views*(n_special+grid_h*grid_w)][channels], dtype
+ *   Vp       same shape and dtype; written. Must not overlap V.
+ *   w        float32 [channels][3][3]; w[c][a+1][b+1] multiplies the value at
+ *            row offset a, column offset b (cross-correlation), zero padding,
+ *            stride 1, no bias; the conv never crosses a view boundary.
+ *
+ * Each patch output is evaluated in float32 as acc = +0; for a = -1..1 (outer),
+ * b = -1..1 (inner): acc = fl(acc + fl(w*v)) — separately rounded, never fused;
+ * then rounded to bf16 (ties to even) in bf16 mode. Special tokens are copied
+ * bit for bit. channels must be a multiple of 8 (bf16) or 4 (f32).
+ * n_views == 0 is a no-op.
+ */
+int vggt3_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, int32_t grid_h,
+                    int32_t grid_w, int32_t n_special, int32_t channels, int32_t dtype,
+                    void* stream);
+
+/*
+ * Bytes of device workspace vggt3_ttt_write / vggt3_ttt_grad need for this
+ * problem (per-chunk fp32 gradient and loss partials of the Eq. 5 split).
+ * Returns 0 for an unsupported shape.
+ */
+size_t vggt3_ttt_workspace_bytes(int64_t n_tokens, int32_t n_heads, int32_t d_head,
+                                 int32_t d_hidden, int32_t dtype);
+
+/*
+ * Write (Update): `steps` full-batch gradient-descent steps of the per-head
+ * inner loss L_h = sum_i (1/d)||T(k_i) - v'_i||^2 ([GRAPH] Eq. 3 with a squared
+ * error; one step = one pass over all n tokens at the current theta, then
+ * theta <- theta - lr * dL/dtheta for all three matrices at once).
+ *
+ *   K, Vp     [n_tokens][C], dtype; read only.
+ *   theta     float32 [n_heads][3*d_head*d_hidden]; read and overwritten with
+ *             theta*. Must not overlap any other argument.
+ *   lr        finite learning rate; steps >= 1 (the released interface's
+ *             default is 1, large scenes use 2).
+ *   workspace device buffer of at least vggt3_ttt_workspace_bytes(...) bytes
+ *             (may be NULL when that is 0).
+ *   loss_out  NULL or float32 [steps][n_heads]: the loss at the theta each
+ *             step starts from.
+ * Supported (d_head, d_hidden): bf16 (64, 128); f32 (16, 32) and (64, 128).
+ * n_tokens == 0 leaves theta unchanged (losses written as 0).
+ */
+int vggt3_ttt_write(const void* K, const void* Vp, float* theta, int64_t n_tokens,
+                    int32_t n_heads, int32_t d_head, int32_t d_hidden, float lr, int32_t steps,
+                    int32_t dtype, void* workspace, size_t workspace_bytes, float* loss_out,
+                    void* stream);
+
+/*
+ * Gradient of the inner loss at theta over n_tokens tokens ([GRAPH] Eq. 5: the
+ * full gradient is the sum of per-minibatch gradients, so chunks of a scene
+ * can be fed in any number of calls with accumulate = 1).
+ *
+ *   grad      float32 [n_heads][3*d_head*d_hidden]; written (accumulate == 0)
+ *             or added to (accumulate != 0). Must not overlap theta.
+ *   loss_out  NULL or float32 [n_heads], written or added to like grad.
+ * Other arguments as in vggt3_ttt_write.
+ */
+int vggt3_ttt_grad(const void* K, const void* Vp, const float* theta, float* grad,
+                   int32_t accumulate, int64_t n_tokens, int32_t n_heads, int32_t d_head,
+                   int32_t d_hidden, int32_t dtype, void* workspace, size_t workspace_bytes,
+                   float* loss_out, void* stream);
+
+/*
+ * The two halves of vggt3_ttt_grad / one step of vggt3_ttt_write, for callers
+ * that schedule them themselves (e.g. to exchange per-chunk partials between
+ * devices, or to time the gradient pass alone). [GRAPH] Eq. 5 writes the
+ * gradient as a sum over minibatches of per-minibatch sums:
+ *
+ * vggt3_ttt_grad_partials: the per-minibatch sums. Writes one fp32 gradient
+ *   partial and one loss partial per (head, token chunk) into `workspace`
+ *   (layout private to the library; size from vggt3_ttt_workspace_bytes).
+ *   The chunking depends only on (n_tokens, n_heads, dtype).
+ *
+ * vggt3_ttt_reduce: the sum over minibatches, by a fixed pairwise tree, then
+ *   mode VGGT3_REDUCE_APPLY:      dst = theta, theta <- theta - lr * g
+ *   mode VGGT3_REDUCE_STORE:      dst = grad,  grad <- g
+ *   mode VGGT3_REDUCE_ACCUMULATE: dst = grad,  grad <- grad + g
+ *   loss_out (NULL or float32 [n_heads]) receives the loss in the same mode
+ *   (APPLY writes it). Arguments (n_tokens, n_heads, d_head, d_hidden, dtype)
+ *   must repeat those of the vggt3_ttt_grad_partials call that filled the
+ *   workspace. With n_tokens == 0: STORE writes zeros, APPLY and ACCUMULATE
+ *   leave dst unchanged.
+ */
+enum { VGGT3_REDUCE_APPLY = 0, VGGT3_REDUCE_STORE = 1, VGGT3_REDUCE_ACCUMULATE = 2 };
+
+int vggt3_ttt_grad_partials(const void* K, const void* Vp, const float* theta, int64_t n_tokens,
+                            int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+int vggt3_ttt_reduce(const void* workspace, size_t workspace_bytes, int64_t n_tokens, int32_t n_heads,
+                     int32_t d_head, int32_t d_hidden, int32_t dtype, int32_t mode, float* dst,
+                     float lr, float* loss_out, void* stream);
+
+/*
+ * One plain gradient-descent update theta <- theta - lr * grad over
+ * n_heads*3*d_head*d_hidden float32 values (applies an accumulated gradient,
+ * [GRAPH] "Large-Scale Inference Strategies"). grad must not overlap theta.
+ */
+int vggt3_ttt_apply(float* theta, const float* grad, float lr, int32_t n_heads, int32_t d_head,
+                    int32_t d_hidden, void* stream);
+
+/*
+ * Read (Apply / query mode): O[i] = T_theta(Q[i]) per head ([GRAPH] Eq. 4;
+ * with a frozen theta* this is the query mode for unseen views).
+ *
+ *   Q         [n_tokens][C], dtype; read only.
+ *   theta     float32 [n_heads][3*d_head*d_hidden]; read only.
+ *   O         [n_tokens][C], dtype; written. Must not overlap Q or theta.
+ * Supported shapes as for vggt3_ttt_write. n_tokens == 0 is a no-op.
+ */
+int vggt3_ttt_read(const void* Q, const float* theta, void* O, int64_t n_tokens, int32_t n_heads,
+                   int32_t d_head, int32_t d_hidden, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VGGT3_H */

@@ -1,0 +1,184 @@
+"""VGG-T^3 test-time-training layer on MI355X (gfx950).
+
+Thin binding over the C ABI in include/vggt3.h (libvggt3.so, built from
+test_layer_amd/csrc). Every function marshals torch tensors (device memory and
+the current stream) into the C calls; all layer arithmetic runs in the HIP
+kernels. There is no CPU or PyTorch fallback: without the built library, or
+without a GPU, calls raise.
+
+    Vp    = shortconv(V, w, n_views, grid_h, grid_w, n_special)
+    theta = ttt_write(K, Vp, theta, lr, steps, n_heads)        # in place
+    O     = ttt_read(Q, theta, n_heads)
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+BF16 = 0
+F32 = 1
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+
+
+class Vggt3Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        lib = _lib.load()
+        detail = lib.vggt3_last_error().decode()
+        super().__init__(f"{fn}: {lib.vggt3_status_str(status).decode()} ({status}): {detail}")
+        self.status = status
+
+
+def lib():
+    return _lib.load()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}; token tensors are bfloat16 or float32")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU (HIP device memory)")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _call(name: str, *args) -> int:
+    rc = getattr(lib(), name)(*args)
+    if rc != OK:
+        raise Vggt3Error(name, rc)
+    return rc
+
+
+def shortconv(V: torch.Tensor, w: torch.Tensor, n_views: int, grid_h: int, grid_w: int, n_special: int,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """V' = depthwise 3x3 ShortConv2D of each view's patch grid; special tokens copied."""
+    if out is None:
+        out = torch.empty_like(V)
+    _check_dev(V, w, out)
+    if w.dtype != torch.float32:
+        raise TypeError("conv weights are float32 [C, 3, 3]")
+    _call("vggt3_shortconv", _ptr(V), _ptr(out), _ptr(w), n_views, grid_h, grid_w, n_special, V.shape[1],
+          _dtype_code(V), _stream())
+    return out
+
+
+def workspace_bytes(n_tokens: int, n_heads: int, d_head: int, d_hidden: int, dtype_code: int) -> int:
+    return int(lib().vggt3_ttt_workspace_bytes(n_tokens, n_heads, d_head, d_hidden, dtype_code))
+
+
+def make_workspace(n_tokens: int, n_heads: int, d_head: int, d_hidden: int, dtype_code: int,
+                   device="cuda") -> Optional[torch.Tensor]:
+    nb = workspace_bytes(n_tokens, n_heads, d_head, d_hidden, dtype_code)
+    if nb == 0:
+        return None
+    return torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+def _mlp_dims(theta: torch.Tensor, X: torch.Tensor, n_heads: int, d_hidden: Optional[int]):
+    C = X.shape[1]
+    if C % n_heads:
+        raise ValueError("channels not divisible by n_heads")
+    d = C // n_heads
+    per = theta.shape[-1] if theta.dim() == 2 else theta.numel() // n_heads
+    m = d_hidden if d_hidden is not None else per // (3 * d)
+    return d, m
+
+
+def ttt_write(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, lr: float, steps: int, n_heads: int,
+              d_hidden: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+              loss_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """`steps` gradient-descent steps of the inner loss; theta (fp32) is updated in place."""
+    _check_dev(K, Vp, theta, workspace, loss_out)
+    d, m = _mlp_dims(theta, K, n_heads, d_hidden)
+    dt = _dtype_code(K)
+    if workspace is None:
+        workspace = make_workspace(K.shape[0], n_heads, d, m, dt, K.device)
+    nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("vggt3_ttt_write", _ptr(K), _ptr(Vp), _ptr(theta), K.shape[0], n_heads, d, m, float(lr), int(steps),
+          dt, _ptr(workspace), nb, _ptr(loss_out), _stream())
+    return theta
+
+
+def ttt_grad(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, n_heads: int,
+             grad: Optional[torch.Tensor] = None, accumulate: bool = False, d_hidden: Optional[int] = None,
+             workspace: Optional[torch.Tensor] = None, loss_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gradient of the inner loss at theta (Eq. 5 split: accumulate=True adds to grad)."""
+    if grad is None:
+        grad = torch.empty_like(theta)
+    _check_dev(K, Vp, theta, grad, workspace, loss_out)
+    d, m = _mlp_dims(theta, K, n_heads, d_hidden)
+    dt = _dtype_code(K)
+    if workspace is None:
+        workspace = make_workspace(K.shape[0], n_heads, d, m, dt, K.device)
+    nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("vggt3_ttt_grad", _ptr(K), _ptr(Vp), _ptr(theta), _ptr(grad), int(bool(accumulate)), K.shape[0],
+          n_heads, d, m, dt, _ptr(workspace), nb, _ptr(loss_out), _stream())
+    return grad
+
+
+REDUCE_APPLY, REDUCE_STORE, REDUCE_ACCUMULATE = 0, 1, 2
+
+
+def ttt_grad_partials(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, n_heads: int,
+                      workspace: torch.Tensor, d_hidden: Optional[int] = None) -> None:
+    """Per-(head, chunk) gradient and loss partials into `workspace` (Eq. 5 inner sums)."""
+    _check_dev(K, Vp, theta, workspace)
+    d, m = _mlp_dims(theta, K, n_heads, d_hidden)
+    _call("vggt3_ttt_grad_partials", _ptr(K), _ptr(Vp), _ptr(theta), K.shape[0], n_heads, d, m, _dtype_code(K),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+
+
+def ttt_reduce(workspace: torch.Tensor, n_tokens: int, n_heads: int, d_head: int, d_hidden: int, dtype_code: int,
+               mode: int, dst: torch.Tensor, lr: float = 0.0, loss_out: Optional[torch.Tensor] = None) -> None:
+    """Fixed-tree sum of the partials, then apply to theta / store / accumulate into dst."""
+    _check_dev(workspace, dst, loss_out)
+    _call("vggt3_ttt_reduce", _ptr(workspace), workspace.numel() * workspace.element_size(), n_tokens, n_heads,
+          d_head, d_hidden, dtype_code, mode, _ptr(dst), float(lr), _ptr(loss_out), _stream())
+
+
+def ttt_apply(theta: torch.Tensor, grad: torch.Tensor, lr: float, n_heads: int, d_head: int,
+              d_hidden: int) -> torch.Tensor:
+    _check_dev(theta, grad)
+    _call("vggt3_ttt_apply", _ptr(theta), _ptr(grad), float(lr), n_heads, d_head, d_hidden, _stream())
+    return theta
+
+
+def ttt_read(Q: torch.Tensor, theta: torch.Tensor, n_heads: int, d_hidden: Optional[int] = None,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """O = T_theta(Q) per head."""
+    if out is None:
+        out = torch.empty_like(Q)
+    _check_dev(Q, theta, out)
+    d, m = _mlp_dims(theta, Q, n_heads, d_hidden)
+    _call("vggt3_ttt_read", _ptr(Q), _ptr(theta), _ptr(out), Q.shape[0], n_heads, d, m, _dtype_code(Q),
+          _stream())
+    return out
+
+
+def ttt_layer(K, V, Q, theta, conv_w, n_views, grid_h, grid_w, n_special, n_heads, lr, steps,
+              workspace=None, loss_out=None, Vp=None, O=None):
+    """The whole layer: V' = ShortConv2D(V); write theta (in place); O = read(Q)."""
+    Vp = shortconv(V, conv_w, n_views, grid_h, grid_w, n_special, out=Vp)
+    ttt_write(K, Vp, theta, lr, steps, n_heads, workspace=workspace, loss_out=loss_out)
+    return ttt_read(Q, theta, n_heads, out=O), Vp

@@ -1,0 +1,338 @@
+// C ABI of the TTT layer: argument validation and launch sequencing.
+// Every check runs on the host before anything is enqueued.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/vggt3.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return VGGT3_OK;
+}
+
+int check_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(VGGT3_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return VGGT3_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  if (a == nullptr || b == nullptr || an == 0 || bn == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+bool valid_dtype(int32_t dt) { return dt == VGGT3_BF16 || dt == VGGT3_F32; }
+size_t elem_size(int32_t dt) { return dt == VGGT3_BF16 ? 2 : 4; }
+
+// Shapes with a kernel in this build.
+bool supported_mlp(int32_t dt, int32_t d, int32_t m) {
+  if (dt == VGGT3_BF16) return d == 64 && m == 128;
+  if (dt == VGGT3_F32) return (d == 16 && m == 32) || (d == 64 && m == 128);
+  return false;
+}
+
+int tile_tokens(int32_t dt) { return dt == VGGT3_BF16 ? 64 : 16; }
+
+struct MlpArgs {
+  int64_t n;
+  int32_t H, d, m, dt;
+};
+
+int check_mlp(const MlpArgs& a) {
+  if (!valid_dtype(a.dt)) return fail(VGGT3_EINVAL, "dtype %d is not VGGT3_BF16 or VGGT3_F32", a.dt);
+  if (a.n < 0) return fail(VGGT3_EINVAL, "n_tokens = %lld < 0", (long long)a.n);
+  if (a.H < 1 || a.d < 1 || a.m < 1)
+    return fail(VGGT3_EINVAL, "n_heads/d_head/d_hidden must be >= 1 (got %d/%d/%d)", a.H, a.d, a.m);
+  if (!supported_mlp(a.dt, a.d, a.m))
+    return fail(VGGT3_EUNSUPPORTED, "no %s kernel for d_head = %d, d_hidden = %d",
+                a.dt == VGGT3_BF16 ? "bf16" : "f32", a.d, a.m);
+  if ((int64_t)a.H * a.d > (int64_t)1 << 20) return fail(VGGT3_EUNSUPPORTED, "too many channels");
+  return VGGT3_OK;
+}
+
+size_t theta_bytes(const MlpArgs& a) { return (size_t)a.H * 3 * a.d * a.m * sizeof(float); }
+size_t token_bytes(const MlpArgs& a) { return (size_t)a.n * a.H * a.d * elem_size(a.dt); }
+
+size_t workspace_bytes(const MlpArgs& a, int* P_out) {
+  const int P = vggt3::ttt_num_chunks(a.n, a.H, tile_tokens(a.dt));
+  if (P_out) *P_out = P;
+  if (a.n == 0) return 0;
+  const size_t part = (size_t)a.H * P * 3 * a.d * a.m * sizeof(float);
+  const size_t loss = (size_t)a.H * P * sizeof(float);
+  return ((part + 255) / 256) * 256 + ((loss + 255) / 256) * 256;
+}
+
+// Gradient over all tokens into (part, loss_part) then reduce in `mode`.
+int run_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& a, void* ws, int P,
+             vggt3::ReduceMode mode, float* dst, float lr, float* loss_out, hipStream_t s) {
+  float* part = static_cast<float*>(ws);
+  const size_t part_bytes = ((size_t)a.H * P * 3 * a.d * a.m * sizeof(float) + 255) / 256 * 256;
+  float* loss_part = reinterpret_cast<float*>(static_cast<char*>(ws) + part_bytes);
+  hipError_t e;
+  if (a.dt == VGGT3_BF16)
+    e = vggt3::launch_grad_partial_bf16(K, Vp, theta, part, loss_part, a.n, a.H, P, s);
+  else
+    e = vggt3::launch_grad_partial_f32(K, Vp, theta, part, loss_part, a.n, a.H, a.d, a.m, P, s);
+  int rc = check_hip(e, "gradient kernel launch");
+  if (rc) return rc;
+  return check_hip(vggt3::launch_reduce(part, loss_part, a.H, P, 3 * a.d * a.m, mode, dst, lr, loss_out, s),
+                   "reduction kernel launch");
+}
+
+int check_workspace(const MlpArgs& a, const void* ws, size_t ws_bytes, int* P) {
+  const size_t need = workspace_bytes(a, P);
+  if (need == 0) return VGGT3_OK;
+  if (ws == nullptr) return fail(VGGT3_EWORKSPACE, "workspace is NULL, %zu bytes needed", need);
+  if (ws_bytes < need) return fail(VGGT3_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(VGGT3_EINVAL, "workspace is not 16-byte aligned");
+  return VGGT3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vggt3_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+const char* vggt3_status_str(int status) {
+  switch (status) {
+    case VGGT3_OK: return "ok";
+    case VGGT3_EINVAL: return "invalid argument";
+    case VGGT3_EUNSUPPORTED: return "unsupported shape or dtype";
+    case VGGT3_EWORKSPACE: return "workspace missing or too small";
+    case VGGT3_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* vggt3_last_error(void) { return g_last_error.c_str(); }
+
+int vggt3_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, int32_t grid_h, int32_t grid_w,
+                    int32_t n_special, int32_t channels, int32_t dtype, void* stream) {
+  if (!valid_dtype(dtype)) return fail(VGGT3_EINVAL, "dtype %d is not VGGT3_BF16 or VGGT3_F32", dtype);
+  if (n_views < 0 || grid_h < 1 || grid_w < 1 || n_special < 0 || channels < 1)
+    return fail(VGGT3_EINVAL, "bad layout: n_views %lld, grid %dx%d, n_special %d, channels %d",
+                (long long)n_views, grid_h, grid_w, n_special, channels);
+  const int vec = dtype == VGGT3_BF16 ? 8 : 4;
+  if (channels % vec != 0)
+    return fail(VGGT3_EUNSUPPORTED, "channels %d is not a multiple of %d", channels, vec);
+  if ((int64_t)grid_h * grid_w > (1 << 24) || n_special > (1 << 20))
+    return fail(VGGT3_EUNSUPPORTED, "view too large");
+  if (n_views == 0) return ok();
+  if (V == nullptr || Vp == nullptr || w == nullptr) return fail(VGGT3_EINVAL, "NULL pointer");
+  if (!aligned16(V) || !aligned16(Vp) || !aligned16(w)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  const size_t bytes = (size_t)n_views * ((size_t)n_special + (size_t)grid_h * grid_w) * channels * elem_size(dtype);
+  if (overlap(V, bytes, Vp, bytes)) return fail(VGGT3_EINVAL, "V' overlaps V (in-place conv is not supported)");
+  if (overlap(w, (size_t)channels * 9 * sizeof(float), Vp, bytes)) return fail(VGGT3_EINVAL, "V' overlaps w");
+  int rc = check_hip(vggt3::launch_shortconv(V, Vp, w, n_views, grid_h, grid_w, n_special, channels,
+                                             dtype == VGGT3_BF16, static_cast<hipStream_t>(stream)),
+                     "shortconv launch");
+  return rc ? rc : ok();
+}
+
+size_t vggt3_ttt_workspace_bytes(int64_t n_tokens, int32_t n_heads, int32_t d_head, int32_t d_hidden,
+                                 int32_t dtype) {
+  const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
+  if (check_mlp(a) != VGGT3_OK) return 0;
+  return workspace_bytes(a, nullptr);
+}
+
+int vggt3_ttt_write(const void* K, const void* Vp, float* theta, int64_t n_tokens, int32_t n_heads, int32_t d_head,
+                    int32_t d_hidden, float lr, int32_t steps, int32_t dtype, void* workspace,
+                    size_t workspace_bytes_, float* loss_out, void* stream) {
+  const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
+  int rc = check_mlp(a);
+  if (rc) return rc;
+  if (!std::isfinite(lr)) return fail(VGGT3_EINVAL, "lr is not finite");
+  if (steps < 1) return fail(VGGT3_EINVAL, "steps = %d < 1", steps);
+  if (theta == nullptr) return fail(VGGT3_EINVAL, "theta is NULL");
+  if (!aligned16(theta) || (loss_out && !aligned16(loss_out)))
+    return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  if (a.n > 0) {
+    if (K == nullptr || Vp == nullptr) return fail(VGGT3_EINVAL, "K or V' is NULL");
+    if (!aligned16(K) || !aligned16(Vp)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  }
+  int P = 1;
+  rc = check_workspace(a, workspace, workspace_bytes_, &P);
+  if (rc) return rc;
+  const size_t tb = theta_bytes(a), xb = token_bytes(a);
+  const size_t lb = loss_out ? (size_t)steps * n_heads * sizeof(float) : 0;
+  if (overlap(theta, tb, K, xb) || overlap(theta, tb, Vp, xb) || overlap(theta, tb, workspace, workspace_bytes_) ||
+      overlap(theta, tb, loss_out, lb))
+    return fail(VGGT3_EINVAL, "theta overlaps another argument");
+  if (overlap(loss_out, lb, workspace, workspace_bytes_) || overlap(loss_out, lb, K, xb) ||
+      overlap(loss_out, lb, Vp, xb))
+    return fail(VGGT3_EINVAL, "loss_out overlaps another argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.n == 0) {
+    if (loss_out) {
+      rc = check_hip(vggt3::launch_fill(loss_out, 0.0f, (int64_t)steps * n_heads, s), "fill launch");
+      if (rc) return rc;
+    }
+    return ok();
+  }
+  for (int st = 0; st < steps; ++st) {
+    rc = run_grad(K, Vp, theta, a, workspace, P, vggt3::kApply, theta, lr,
+                  loss_out ? loss_out + (size_t)st * n_heads : nullptr, s);
+    if (rc) return rc;
+  }
+  return ok();
+}
+
+int vggt3_ttt_grad(const void* K, const void* Vp, const float* theta, float* grad, int32_t accumulate,
+                   int64_t n_tokens, int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t dtype,
+                   void* workspace, size_t workspace_bytes_, float* loss_out, void* stream) {
+  const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
+  int rc = check_mlp(a);
+  if (rc) return rc;
+  if (theta == nullptr || grad == nullptr) return fail(VGGT3_EINVAL, "theta or grad is NULL");
+  if (!aligned16(theta) || !aligned16(grad) || (loss_out && !aligned16(loss_out)))
+    return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  if (a.n > 0) {
+    if (K == nullptr || Vp == nullptr) return fail(VGGT3_EINVAL, "K or V' is NULL");
+    if (!aligned16(K) || !aligned16(Vp)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  }
+  int P = 1;
+  rc = check_workspace(a, workspace, workspace_bytes_, &P);
+  if (rc) return rc;
+  const size_t tb = theta_bytes(a), xb = token_bytes(a);
+  const size_t lb = loss_out ? (size_t)n_heads * sizeof(float) : 0;
+  if (overlap(grad, tb, theta, tb) || overlap(grad, tb, K, xb) || overlap(grad, tb, Vp, xb) ||
+      overlap(grad, tb, workspace, workspace_bytes_) || overlap(grad, tb, loss_out, lb))
+    return fail(VGGT3_EINVAL, "grad overlaps another argument");
+  if (overlap(loss_out, lb, workspace, workspace_bytes_) || overlap(loss_out, lb, theta, tb))
+    return fail(VGGT3_EINVAL, "loss_out overlaps another argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.n == 0) {
+    if (!accumulate) {
+      rc = check_hip(vggt3::launch_fill(grad, 0.0f, (int64_t)tb / 4, s), "fill launch");
+      if (!rc && loss_out) rc = check_hip(vggt3::launch_fill(loss_out, 0.0f, n_heads, s), "fill launch");
+      if (rc) return rc;
+    }
+    return ok();
+  }
+  rc = run_grad(K, Vp, theta, a, workspace, P, accumulate ? vggt3::kAccum : vggt3::kStore, grad, 0.0f, loss_out,
+                s);
+  return rc ? rc : ok();
+}
+
+int vggt3_ttt_grad_partials(const void* K, const void* Vp, const float* theta, int64_t n_tokens, int32_t n_heads,
+                            int32_t d_head, int32_t d_hidden, int32_t dtype, void* workspace,
+                            size_t workspace_bytes_, void* stream) {
+  const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
+  int rc = check_mlp(a);
+  if (rc) return rc;
+  if (theta == nullptr) return fail(VGGT3_EINVAL, "theta is NULL");
+  if (!aligned16(theta)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  if (a.n == 0) return ok();
+  if (K == nullptr || Vp == nullptr) return fail(VGGT3_EINVAL, "K or V' is NULL");
+  if (!aligned16(K) || !aligned16(Vp)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  int P = 1;
+  rc = check_workspace(a, workspace, workspace_bytes_, &P);
+  if (rc) return rc;
+  const size_t tb = theta_bytes(a), xb = token_bytes(a);
+  if (overlap(workspace, workspace_bytes_, theta, tb) || overlap(workspace, workspace_bytes_, K, xb) ||
+      overlap(workspace, workspace_bytes_, Vp, xb))
+    return fail(VGGT3_EINVAL, "workspace overlaps another argument");
+  float* part = static_cast<float*>(workspace);
+  const size_t part_bytes = ((size_t)a.H * P * 3 * a.d * a.m * sizeof(float) + 255) / 256 * 256;
+  float* loss_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = a.dt == VGGT3_BF16
+                     ? vggt3::launch_grad_partial_bf16(K, Vp, theta, part, loss_part, a.n, a.H, P, s)
+                     : vggt3::launch_grad_partial_f32(K, Vp, theta, part, loss_part, a.n, a.H, a.d, a.m, P, s);
+  rc = check_hip(e, "gradient kernel launch");
+  return rc ? rc : ok();
+}
+
+int vggt3_ttt_reduce(const void* workspace, size_t workspace_bytes_, int64_t n_tokens, int32_t n_heads,
+                     int32_t d_head, int32_t d_hidden, int32_t dtype, int32_t mode, float* dst, float lr,
+                     float* loss_out, void* stream) {
+  const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
+  int rc = check_mlp(a);
+  if (rc) return rc;
+  if (mode != VGGT3_REDUCE_APPLY && mode != VGGT3_REDUCE_STORE && mode != VGGT3_REDUCE_ACCUMULATE)
+    return fail(VGGT3_EINVAL, "unknown reduce mode %d", mode);
+  if (!std::isfinite(lr)) return fail(VGGT3_EINVAL, "lr is not finite");
+  if (dst == nullptr) return fail(VGGT3_EINVAL, "dst is NULL");
+  if (!aligned16(dst) || (loss_out && !aligned16(loss_out))) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  const size_t tb = theta_bytes(a);
+  const size_t lb = loss_out ? (size_t)n_heads * sizeof(float) : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.n == 0) {
+    if (mode == VGGT3_REDUCE_STORE) {
+      rc = check_hip(vggt3::launch_fill(dst, 0.0f, (int64_t)tb / 4, s), "fill launch");
+      if (!rc && loss_out) rc = check_hip(vggt3::launch_fill(loss_out, 0.0f, n_heads, s), "fill launch");
+      if (rc) return rc;
+    }
+    return ok();
+  }
+  int P = 1;
+  rc = check_workspace(a, workspace, workspace_bytes_, &P);
+  if (rc) return rc;
+  if (overlap(dst, tb, workspace, workspace_bytes_) || overlap(loss_out, lb, workspace, workspace_bytes_) ||
+      overlap(dst, tb, loss_out, lb))
+    return fail(VGGT3_EINVAL, "dst or loss_out overlaps another argument");
+  const float* part = static_cast<const float*>(workspace);
+  const size_t part_bytes = ((size_t)a.H * P * 3 * a.d * a.m * sizeof(float) + 255) / 256 * 256;
+  const float* loss_part = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + part_bytes);
+  const vggt3::ReduceMode rm = mode == VGGT3_REDUCE_APPLY   ? vggt3::kApply
+                               : mode == VGGT3_REDUCE_STORE ? vggt3::kStore
+                                                            : vggt3::kAccum;
+  rc = check_hip(vggt3::launch_reduce(part, loss_part, a.H, P, 3 * a.d * a.m, rm, dst, lr, loss_out, s),
+                 "reduction kernel launch");
+  return rc ? rc : ok();
+}
+
+int vggt3_ttt_apply(float* theta, const float* grad, float lr, int32_t n_heads, int32_t d_head, int32_t d_hidden,
+                    void* stream) {
+  if (n_heads < 0 || d_head < 1 || d_hidden < 1) return fail(VGGT3_EINVAL, "bad shape");
+  if (!std::isfinite(lr)) return fail(VGGT3_EINVAL, "lr is not finite");
+  const int64_t count = (int64_t)n_heads * 3 * d_head * d_hidden;
+  if (count == 0) return ok();
+  if (theta == nullptr || grad == nullptr) return fail(VGGT3_EINVAL, "theta or grad is NULL");
+  if (!aligned16(theta) || !aligned16(grad)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  if (overlap(theta, count * 4, grad, count * 4)) return fail(VGGT3_EINVAL, "grad overlaps theta");
+  int rc = check_hip(vggt3::launch_apply(theta, grad, lr, count, static_cast<hipStream_t>(stream)), "apply launch");
+  return rc ? rc : ok();
+}
+
+int vggt3_ttt_read(const void* Q, const float* theta, void* O, int64_t n_tokens, int32_t n_heads, int32_t d_head,
+                   int32_t d_hidden, int32_t dtype, void* stream) {
+  const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
+  int rc = check_mlp(a);
+  if (rc) return rc;
+  if (a.n == 0) return ok();
+  if (Q == nullptr || theta == nullptr || O == nullptr) return fail(VGGT3_EINVAL, "NULL pointer");
+  if (!aligned16(Q) || !aligned16(theta) || !aligned16(O)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  const size_t tb = theta_bytes(a), xb = token_bytes(a);
+  if (overlap(O, xb, Q, xb) || overlap(O, xb, theta, tb)) return fail(VGGT3_EINVAL, "O overlaps Q or theta");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == VGGT3_BF16 ? vggt3::launch_read_bf16(Q, theta, O, a.n, a.H, s)
+                                     : vggt3::launch_read_f32(Q, theta, O, a.n, a.H, a.d, a.m, s);
+  rc = check_hip(e, "read kernel launch");
+  return rc ? rc : ok();
+}
+
+}  // extern "C"

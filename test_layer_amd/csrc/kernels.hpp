@@ -1,0 +1,54 @@
+// Internal launchers of the TTT-layer kernels (host side) and launch helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vggt3 {
+
+// The dispatcher hands workgroup b to XCD b % 8 (8 XCDs, each with its own L2).
+// Remap so that each XCD processes a contiguous range of logical workgroups:
+// neighbouring tiles (which share halo rows or weights) then share one L2.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t n) {
+  const int64_t q = n / kNumXcd, r = n % kNumXcd;
+  const int64_t xcd = b % kNumXcd, idx = b / kNumXcd;
+  return xcd * q + (xcd < r ? xcd : r) + idx;
+}
+
+// Chunking of the Eq. 5 gradient split: the tokens are cut into P chunks
+// (P a power of two, a function of n_tokens and n_heads only, never of the
+// device), one workgroup per (head, chunk); partial gradients are summed by a
+// fixed pairwise tree, so results do not depend on the GPU's CU count.
+constexpr int kMaxChunks = 64;
+int ttt_num_chunks(int64_t n_tokens, int n_heads, int tile_tokens);
+
+hipError_t launch_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, int grid_h,
+                            int grid_w, int n_special, int C, bool bf16, hipStream_t stream);
+
+// Per-(head, chunk) fp32 gradient and loss partials.
+// part: [n_heads][P][3*d*m], loss_part: [n_heads][P].
+hipError_t launch_grad_partial_bf16(const void* K, const void* Vp, const float* theta, float* part,
+                                    float* loss_part, int64_t n_tokens, int n_heads, int P,
+                                    hipStream_t stream);
+hipError_t launch_grad_partial_f32(const void* K, const void* Vp, const float* theta, float* part,
+                                   float* loss_part, int64_t n_tokens, int n_heads, int d, int m, int P,
+                                   hipStream_t stream);
+
+// Fixed-tree reduction of the partials, then (mode) either
+//   kApply:   theta -= lr * g            (write step), loss_out[h] = loss
+//   kStore:   grad = g,  loss_out = loss
+//   kAccum:   grad += g, loss_out += loss
+enum ReduceMode { kApply = 0, kStore = 1, kAccum = 2 };
+hipError_t launch_reduce(const float* part, const float* loss_part, int n_heads, int P, int per_head,
+                         ReduceMode mode, float* theta_or_grad, float lr, float* loss_out,
+                         hipStream_t stream);
+hipError_t launch_apply(float* theta, const float* grad, float lr, int64_t count, hipStream_t stream);
+hipError_t launch_fill(float* dst, float value, int64_t count, hipStream_t stream);
+
+hipError_t launch_read_bf16(const void* Q, const float* theta, void* O, int64_t n_tokens, int n_heads,
+                            hipStream_t stream);
+hipError_t launch_read_f32(const void* Q, const float* theta, void* O, int64_t n_tokens, int n_heads,
+                           int d, int m, hipStream_t stream);
+
+}  // namespace vggt3

@@ -1,0 +1,146 @@
+"""The C ABI loads, exports every declared symbol, and validates arguments on
+the host before touching the GPU (CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import test_layer_amd as tla
+from test_layer_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vggt3.h")
+
+# a fake, 16-byte aligned "device" address: validation must reject before use
+FAKE = ctypes.c_void_p(0x10000)
+FAKE2 = ctypes.c_void_p(0x20000000)
+FAKE3 = ctypes.c_void_p(0x40000000)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vggt3_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"{n} has no ctypes signature"
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, 7):
+        assert lib.vggt3_status_str(code)
+    assert lib.vggt3_version() >= 10000
+
+
+def test_workspace_bytes(lib):
+    nb = lib.vggt3_ttt_workspace_bytes(1_374_000, 16, 64, 128, tla.BF16)
+    assert nb >= 16 * 3 * 64 * 128 * 4  # at least one fp32 partial per head
+    assert nb < 256 << 20
+    assert lib.vggt3_ttt_workspace_bytes(0, 16, 64, 128, tla.BF16) == 0
+    assert lib.vggt3_ttt_workspace_bytes(100, 16, 32, 128, tla.BF16) == 0  # unsupported
+    assert lib.vggt3_ttt_workspace_bytes(128, 1, 16, 32, tla.F32) > 0
+    assert lib.vggt3_ttt_workspace_bytes(100, 1, 16, 32, 9) == 0
+    # chunking depends only on (n, heads, dtype): monotone, bounded
+    a = lib.vggt3_ttt_workspace_bytes(1000, 16, 64, 128, tla.BF16)
+    b = lib.vggt3_ttt_workspace_bytes(10_000_000, 16, 64, 128, tla.BF16)
+    assert 0 < a <= b
+
+
+def _err(lib):
+    return lib.vggt3_last_error().decode()
+
+
+def test_shortconv_validation(lib):
+    ok_args = dict(V=FAKE, Vp=FAKE2, w=FAKE3, n=2, gh=37, gw=37, ns=5, C=1024, dt=tla.BF16)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return lib.vggt3_shortconv(a["V"], a["Vp"], a["w"], a["n"], a["gh"], a["gw"], a["ns"], a["C"], a["dt"], None)
+
+    assert call(dt=5) == tla.EINVAL
+    assert call(n=-1) == tla.EINVAL
+    assert call(gh=0) == tla.EINVAL
+    assert call(ns=-1) == tla.EINVAL
+    assert call(C=12) == tla.EUNSUPPORTED  # not a multiple of 8 in bf16
+    assert call(V=None) == tla.EINVAL
+    assert call(V=ctypes.c_void_p(0x10008)) == tla.EINVAL  # misaligned
+    assert call(Vp=FAKE) == tla.EINVAL and "overlap" in _err(lib)  # in place
+    assert call(n=0) == tla.OK  # empty scene: no-op, nothing enqueued
+
+
+def test_write_validation(lib):
+    n, H, d, m = 4096, 16, 64, 128
+    ws_need = lib.vggt3_ttt_workspace_bytes(n, H, d, m, tla.BF16)
+
+    def call(K=FAKE, Vp=FAKE2, theta=FAKE3, n=n, H=H, d=d, m=m, lr=0.1, steps=1, dt=tla.BF16,
+             ws=ctypes.c_void_p(0x60000000), wsb=ws_need, loss=None):
+        return lib.vggt3_ttt_write(K, Vp, theta, n, H, d, m, lr, steps, dt, ws, wsb, loss, None)
+
+    assert call(steps=0) == tla.EINVAL
+    assert call(lr=float("nan")) == tla.EINVAL
+    assert call(lr=float("inf")) == tla.EINVAL
+    assert call(n=-5) == tla.EINVAL
+    assert call(d=32) == tla.EUNSUPPORTED
+    assert call(m=64) == tla.EUNSUPPORTED
+    assert call(dt=tla.F32, d=16, m=64) == tla.EUNSUPPORTED
+    assert call(theta=None) == tla.EINVAL
+    assert call(K=None) == tla.EINVAL
+    assert call(ws=None) == tla.EWORKSPACE
+    assert call(wsb=ws_need - 1) == tla.EWORKSPACE
+    assert call(theta=FAKE) == tla.EINVAL and "overlap" in _err(lib)
+    assert call(theta=ctypes.c_void_p(0x40000004)) == tla.EINVAL  # misaligned
+    assert call(H=0) == tla.EINVAL
+    # empty scene with no loss output: nothing to do, nothing enqueued
+    assert call(n=0, K=None, Vp=None, ws=None, wsb=0) == tla.OK
+
+
+def test_grad_reduce_apply_read_validation(lib):
+    n, H, d, m = 4096, 16, 64, 128
+    wsb = lib.vggt3_ttt_workspace_bytes(n, H, d, m, tla.BF16)
+    ws = ctypes.c_void_p(0x60000000)
+    assert lib.vggt3_ttt_grad(FAKE, FAKE2, FAKE3, FAKE3, 0, n, H, d, m, tla.BF16, ws, wsb, None, None) == tla.EINVAL
+    assert lib.vggt3_ttt_grad(FAKE, FAKE2, FAKE3, None, 0, n, H, d, m, tla.BF16, ws, wsb, None, None) == tla.EINVAL
+    assert lib.vggt3_ttt_grad(FAKE, FAKE2, FAKE3, ctypes.c_void_p(0x70000000), 0, n, H, d, m, tla.BF16, ws, 16,
+                              None, None) == tla.EWORKSPACE
+    assert lib.vggt3_ttt_grad_partials(FAKE, FAKE2, FAKE3, n, H, d, m, tla.BF16, None, 0, None) == tla.EWORKSPACE
+    assert lib.vggt3_ttt_grad_partials(FAKE, FAKE2, FAKE3, n, H, 48, m, tla.BF16, ws, wsb, None) == tla.EUNSUPPORTED
+    assert lib.vggt3_ttt_reduce(ws, wsb, n, H, d, m, tla.BF16, 3, FAKE3, 0.1, None, None) == tla.EINVAL
+    assert lib.vggt3_ttt_reduce(ws, wsb, n, H, d, m, tla.BF16, 0, None, 0.1, None, None) == tla.EINVAL
+    assert lib.vggt3_ttt_reduce(ws, wsb, n, H, d, m, tla.BF16, 0, ws, 0.1, None, None) == tla.EINVAL
+    assert lib.vggt3_ttt_apply(FAKE, FAKE, 0.1, H, d, m, None) == tla.EINVAL
+    assert lib.vggt3_ttt_apply(FAKE, FAKE2, float("nan"), H, d, m, None) == tla.EINVAL
+    assert lib.vggt3_ttt_apply(FAKE, FAKE2, 0.1, 0, d, m, None) == tla.OK  # nothing to update
+    assert lib.vggt3_ttt_read(FAKE, FAKE3, FAKE, n, H, d, m, tla.BF16, None) == tla.EINVAL
+    assert lib.vggt3_ttt_read(FAKE, FAKE3, FAKE2, n, H, d, 96, tla.BF16, None) == tla.EUNSUPPORTED
+    assert lib.vggt3_ttt_read(None, FAKE3, FAKE2, n, H, d, m, tla.BF16, None) == tla.EINVAL
+    assert lib.vggt3_ttt_read(None, None, None, 0, H, d, m, tla.BF16, None) == tla.OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    V = torch.zeros(10, 16)
+    w = torch.zeros(16, 3, 3)
+    with pytest.raises(ValueError):
+        tla.shortconv(V, w, 1, 3, 3, 1)
+
+
+def test_product_path_does_not_import_oracle():
+    """The package never reaches for the CPU oracle (no fallback)."""
+    pkg = os.path.join(ROOT, "test_layer_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, flags=re.M), f

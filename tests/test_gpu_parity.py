@@ -1,0 +1,284 @@
+"""Parity of the HIP path against the CPU oracle on identical seeded inputs.
+
+Bar (per head, normwise max error max|x - x_ref| / max|x_ref|):
+  * ShortConv2D: bit-exact (the fp32 conv contract, bf16 round to nearest even);
+  * bf16 compute: theta*, delta-theta = theta* - theta0, gradients and read
+    outputs within 2e-2;
+  * fp32 compute: within 1e-4.
+The oracle always computes its own V' from V and its own theta* from theta0;
+nothing it consumes comes from the HIP path.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import test_layer_amd as tla
+from synth import CONFIGS, make_inputs
+from tests.gpu_util import bits, f32_to_bits, rel_err, rel_err_per_head, to64
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+TOL_F32 = 1e-4
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tla.lib()
+
+
+def _small_vggt(views=3, steps=2, heads=16, dtype="bf16", **kw):
+    from dataclasses import replace
+    return replace(CONFIGS["views24"], n_views=views, steps=steps, n_heads=heads, dtype=dtype,
+                   name=f"vggt{views}v{heads}h", **kw)
+
+
+def _conv(inp):
+    c = inp.cfg
+    return tla.shortconv(inp.V, inp.conv_w, c.n_views, c.grid_h, c.grid_w, c.n_special)
+
+
+def _oracle_conv(inp, out):
+    c = inp.cfg
+    return oracle.shortconv(to64(inp.V).astype(np.float32), inp.conv_w.cpu().numpy(), c.n_views, c.grid_h,
+                            c.grid_w, c.n_special, out=out)
+
+
+# ----------------------------------------------------------------------------
+# ShortConv2D
+# ----------------------------------------------------------------------------
+
+CONV_CASES = [
+    # (views, grid_h, grid_w, n_special, heads, d_head, dtype)
+    (2, 8, 8, 0, 1, 16, "f32"),
+    (3, 37, 37, 5, 16, 64, "bf16"),
+    (2, 5, 7, 2, 1, 64, "bf16"),
+    (1, 1, 1, 1, 1, 8, "bf16"),
+    (4, 3, 2, 0, 2, 4, "f32"),
+    (2, 37, 37, 5, 4, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_shortconv_bitexact(case):
+    from dataclasses import replace
+    views, gh, gw, ns, H, d, dt = case
+    cfg = replace(CONFIGS["tiny_f32"], n_views=views, grid_h=gh, grid_w=gw, n_special=ns, n_heads=H, d_head=d,
+                  d_hidden=2 * d, dtype=dt, normalize=(dt == "bf16"), name="conv")
+    print(f"[conv] {case}", flush=True)
+    inp = make_inputs(cfg, DEV, with_q=False)
+    Vp = _conv(inp)
+    torch.cuda.synchronize()
+    ref = _oracle_conv(inp, "bf16" if dt == "bf16" else "f32")
+    np.testing.assert_array_equal(bits(Vp), f32_to_bits(ref, dt == "bf16"))
+
+
+def test_shortconv_special_tokens_and_edges_bitexact():
+    """Extreme values: subnormal products, signed zeros and large magnitudes follow the contract."""
+    from dataclasses import replace
+    cfg = replace(CONFIGS["tiny_f32"], n_views=2, grid_h=6, grid_w=5, n_special=3, n_heads=2, d_head=16,
+                  dtype="f32", name="conv-edge")
+    inp = make_inputs(cfg, DEV, with_q=False)
+    V = inp.V.clone()
+    V[::3] *= 1e-38  # products land in the subnormal range
+    V[1::7] = -0.0
+    V[2::5] *= 1e30
+    inp.V.copy_(V)
+    Vp = _conv(inp)
+    ref = _oracle_conv(inp, "f32")
+    np.testing.assert_array_equal(bits(Vp), f32_to_bits(ref, False))
+
+
+# ----------------------------------------------------------------------------
+# Read
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_tokens", [1, 31, 1000, 4122])
+def test_read_bf16_parity(n_tokens):
+    cfg = _small_vggt(views=3)
+    print(f"[read bf16] n={n_tokens}", flush=True)
+    inp = make_inputs(cfg, DEV)
+    Q = inp.Q[:n_tokens].contiguous()
+    O = tla.ttt_read(Q, inp.theta0, cfg.n_heads)
+    ref = oracle.ttt_read(to64(Q), inp.theta0.cpu().numpy(), cfg.n_heads, cfg.d_head, cfg.d_hidden)
+    err = rel_err_per_head(to64(O), ref, cfg.n_heads)
+    assert err.max() <= TOL_BF16, err
+
+
+def test_read_bf16_trained_weights_parity():
+    """A theta far from init (large weights) still matches: exercises the whole sigmoid range."""
+    cfg = _small_vggt(views=2, heads=4)
+    inp = make_inputs(cfg, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7)
+    theta = torch.randn(inp.theta0.shape, generator=g, device=DEV) * 0.5
+    O = tla.ttt_read(inp.Q, theta, cfg.n_heads)
+    ref = oracle.ttt_read(to64(inp.Q), theta.cpu().numpy(), cfg.n_heads, cfg.d_head, cfg.d_hidden)
+    err = rel_err_per_head(to64(O), ref, cfg.n_heads)
+    assert err.max() <= TOL_BF16, err
+
+
+# ----------------------------------------------------------------------------
+# Write (gradient, steps) in bf16
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_tokens", [1, 64, 100, 4122])
+def test_grad_bf16_parity(n_tokens):
+    cfg = _small_vggt(views=3)
+    print(f"[grad bf16] n={n_tokens}", flush=True)
+    inp = make_inputs(cfg, DEV, with_q=False)
+    Vp = _conv(inp)
+    K = inp.K[:n_tokens].contiguous()
+    Vs = Vp[:n_tokens].contiguous()
+    loss = torch.empty(cfg.n_heads, device=DEV)
+    g = tla.ttt_grad(K, Vs, inp.theta0, cfg.n_heads, loss_out=loss)
+    Vp_ref = _oracle_conv(inp, "bf16")[:n_tokens]
+    g_ref, L_ref = oracle.ttt_grad(to64(K), Vp_ref.astype(np.float64), inp.theta0.cpu().numpy(), cfg.n_heads,
+                                   cfg.d_head, cfg.d_hidden)
+    err = rel_err_per_head(to64(g), g_ref, cfg.n_heads, axis_cols=False)
+    assert err.max() <= TOL_BF16, err
+    lerr = np.abs(loss.cpu().numpy() - L_ref) / np.abs(L_ref)
+    assert lerr.max() <= TOL_BF16, lerr
+
+
+def test_write_bf16_parity_two_steps():
+    cfg = _small_vggt(views=3, steps=2)
+    inp = make_inputs(cfg, DEV, with_q=True)
+    Vp = _conv(inp)
+    theta = inp.theta0.clone()
+    loss = torch.empty((cfg.steps, cfg.n_heads), device=DEV)
+    tla.ttt_write(inp.K, Vp, theta, cfg.lr, cfg.steps, cfg.n_heads, loss_out=loss)
+    O = tla.ttt_read(inp.Q, theta, cfg.n_heads)
+    th0 = inp.theta0.cpu().numpy()
+    Vp_ref = _oracle_conv(inp, "bf16").astype(np.float64)
+    th_ref, L_ref, _ = oracle.ttt_write(to64(inp.K), Vp_ref, th0, cfg.n_heads, cfg.d_head, cfg.d_hidden, cfg.lr,
+                                        cfg.steps)
+    th = theta.cpu().numpy().astype(np.float64)
+    assert rel_err_per_head(th, th_ref, cfg.n_heads, axis_cols=False).max() <= TOL_BF16
+    dth = rel_err_per_head(th - th0, th_ref - th0, cfg.n_heads, axis_cols=False)
+    assert dth.max() <= TOL_BF16, dth
+    lerr = np.abs(loss.cpu().numpy() - L_ref) / np.abs(L_ref)
+    assert lerr.max() <= TOL_BF16, lerr
+    O_ref = oracle.ttt_read(to64(inp.Q), th_ref, cfg.n_heads, cfg.d_head, cfg.d_hidden)
+    assert rel_err_per_head(to64(O), O_ref, cfg.n_heads).max() <= TOL_BF16
+
+
+def test_write_equals_partials_then_reduce_bitwise():
+    cfg = _small_vggt(views=2, steps=2, heads=4)
+    inp = make_inputs(cfg, DEV, with_q=False)
+    Vp = _conv(inp)
+    a = inp.theta0.clone()
+    tla.ttt_write(inp.K, Vp, a, cfg.lr, cfg.steps, cfg.n_heads)
+    b = inp.theta0.clone()
+    ws = tla.make_workspace(cfg.n_tokens, cfg.n_heads, cfg.d_head, cfg.d_hidden, tla.BF16)
+    for _ in range(cfg.steps):
+        tla.ttt_grad_partials(inp.K, Vp, b, cfg.n_heads, ws)
+        tla.ttt_reduce(ws, cfg.n_tokens, cfg.n_heads, cfg.d_head, cfg.d_hidden, tla.BF16, tla.REDUCE_APPLY, b,
+                       cfg.lr)
+    np.testing.assert_array_equal(bits(a), bits(b))
+    # grad + apply reproduces the fused step as well (same tree, then theta - lr*g)
+    c = inp.theta0.clone()
+    for _ in range(cfg.steps):
+        g = tla.ttt_grad(inp.K, Vp, c, cfg.n_heads)
+        tla.ttt_apply(c, g, cfg.lr, cfg.n_heads, cfg.d_head, cfg.d_hidden)
+    np.testing.assert_array_equal(bits(a), bits(c))
+
+
+def test_eq5_chunked_gradient_on_gpu():
+    """Gradient over all tokens == sum of gradients over two token ranges (accumulate)."""
+    cfg = _small_vggt(views=3, heads=4)
+    inp = make_inputs(cfg, DEV, with_q=False)
+    Vp = _conv(inp)
+    full = tla.ttt_grad(inp.K, Vp, inp.theta0, cfg.n_heads)
+    cut = 1500
+    part = tla.ttt_grad(inp.K[:cut].contiguous(), Vp[:cut].contiguous(), inp.theta0, cfg.n_heads)
+    tla.ttt_grad(inp.K[cut:].contiguous(), Vp[cut:].contiguous(), inp.theta0, cfg.n_heads, grad=part,
+                 accumulate=True)
+    err = rel_err_per_head(to64(part), to64(full), cfg.n_heads, axis_cols=False)
+    assert err.max() <= 1e-5, err
+
+
+def test_determinism_bitwise():
+    cfg = _small_vggt(views=3, steps=2)
+    inp = make_inputs(cfg, DEV)
+    outs = []
+    for _ in range(2):
+        Vp = _conv(inp)
+        th = inp.theta0.clone()
+        tla.ttt_write(inp.K, Vp, th, cfg.lr, cfg.steps, cfg.n_heads)
+        O = tla.ttt_read(inp.Q, th, cfg.n_heads)
+        outs.append((bits(Vp), bits(th), bits(O)))
+    for x, y in zip(*outs):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_empty_scene_and_single_token():
+    cfg = _small_vggt(views=1, heads=2)
+    inp = make_inputs(cfg, DEV)
+    th = inp.theta0.clone()
+    loss = torch.full((2, cfg.n_heads), 7.0, device=DEV)
+    tla.ttt_write(inp.K[:0], inp.V[:0], th, 0.1, 2, cfg.n_heads, loss_out=loss)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(th), bits(inp.theta0))
+    assert torch.all(loss == 0)
+    O = tla.ttt_read(inp.Q[:0], th, cfg.n_heads)
+    assert O.shape[0] == 0
+    g = tla.ttt_grad(inp.K[:0], inp.V[:0], th, cfg.n_heads)
+    assert torch.all(g == 0)
+    # one token
+    Vp = _conv(inp)
+    K1, V1 = inp.K[:1].contiguous(), Vp[:1].contiguous()
+    tla.ttt_write(K1, V1, th, 0.1, 1, cfg.n_heads)
+    ref, _, _ = oracle.ttt_write(to64(K1), to64(V1), inp.theta0.cpu().numpy(), cfg.n_heads, cfg.d_head,
+                                 cfg.d_hidden, 0.1, 1)
+    th0 = inp.theta0.cpu().numpy()
+    d = rel_err_per_head(th.cpu().numpy() - th0, ref - th0, cfg.n_heads, axis_cols=False)
+    assert d.max() <= TOL_BF16, d
+
+
+# ----------------------------------------------------------------------------
+# fp32 mode
+# ----------------------------------------------------------------------------
+
+def test_tiny_f32_layer_parity():
+    """2 views of 8x8 patches, 1 head, d 16, hidden 32, fp32, 1 step, then the read."""
+    cfg = CONFIGS["tiny_f32"]
+    inp = make_inputs(cfg, DEV)
+    Vp = _conv(inp)
+    theta = inp.theta0.clone()
+    loss = torch.empty((cfg.steps, cfg.n_heads), device=DEV)
+    tla.ttt_write(inp.K, Vp, theta, cfg.lr, cfg.steps, cfg.n_heads, loss_out=loss)
+    O = tla.ttt_read(inp.Q, theta, cfg.n_heads)
+    th0 = inp.theta0.cpu().numpy()
+    Vp_ref = _oracle_conv(inp, "f32")
+    np.testing.assert_array_equal(bits(Vp), f32_to_bits(Vp_ref, False))
+    th_ref, L_ref, _ = oracle.ttt_write(to64(inp.K), Vp_ref.astype(np.float64), th0, 1, 16, 32, cfg.lr, cfg.steps)
+    th = theta.cpu().numpy().astype(np.float64)
+    assert rel_err(th, th_ref) <= TOL_F32
+    assert rel_err(th - th0, th_ref - th0) <= TOL_F32
+    assert abs(loss.item() - L_ref[0, 0]) / L_ref[0, 0] <= TOL_F32
+    O_ref = oracle.ttt_read(to64(inp.Q), th_ref, 1, 16, 32)
+    assert rel_err(to64(O), O_ref) <= TOL_F32
+
+
+def test_f32_vggt_shape_parity():
+    cfg = _small_vggt(views=2, heads=2, dtype="f32", steps=2)
+    inp = make_inputs(cfg, DEV)
+    Vp = _conv(inp)
+    theta = inp.theta0.clone()
+    tla.ttt_write(inp.K, Vp, theta, cfg.lr, cfg.steps, cfg.n_heads)
+    O = tla.ttt_read(inp.Q, theta, cfg.n_heads)
+    th0 = inp.theta0.cpu().numpy()
+    Vp_ref = _oracle_conv(inp, "f32").astype(np.float64)
+    th_ref, _, _ = oracle.ttt_write(to64(inp.K), Vp_ref, th0, cfg.n_heads, 64, 128, cfg.lr, cfg.steps)
+    th = theta.cpu().numpy().astype(np.float64)
+    assert rel_err_per_head(th - th0, th_ref - th0, cfg.n_heads, axis_cols=False).max() <= TOL_F32
+    O_ref = oracle.ttt_read(to64(inp.Q), th_ref, cfg.n_heads, 64, 128)
+    assert rel_err_per_head(to64(O), O_ref, cfg.n_heads).max() <= TOL_F32
