@@ -1,0 +1,142 @@
+// Read pass (bf16 MFMA): O = T_theta(Q) per head for d = 64, m = 128.
+//
+// Query step of the fast-weight MLP (paper-graph summary "VGG-T3: Offline
+// Feed-Forward 3D Reconstruction at Scale", section 3.4, Eq. 4: o_i =
+// T_theta(q_i); with a frozen theta* this is also the query mode for unseen
+// views), T(x) = (silu(x W_g) * (x W_u)) W_d without biases.
+#include "bf16_ops.hpp"
+#include "kernels.hpp"
+
+namespace vggt3 {
+namespace {
+
+constexpr int D = 64;
+constexpr int M = 128;
+constexpr int KP = D + 8;
+constexpr int HP = M + 8;
+constexpr int DM = D * M;
+constexpr int PER_HEAD = 3 * DM;
+
+// ---------------------------------------------------------------------------
+// Read pass O = T(Q) per head. Tokens run across lanes here (MFMA columns),
+// so the chain G^T = W_g^T Q^T -> H^T -> Y^T = W_d^T H^T contracts over e and
+// then over hidden units with no transposes: each H^T tile is consumed from
+// registers. Weights sit in LDS, pre-permuted to match the operand orders.
+// Each wave handles 32 tokens per iteration.
+// ---------------------------------------------------------------------------
+constexpr int RT = 32;  // tokens per wave iteration
+
+__global__ __launch_bounds__(256, 2) void read_bf16_kernel(const uint16_t* __restrict__ Q,
+                                                           const float* __restrict__ theta,
+                                                           uint16_t* __restrict__ O, int64_t n_tokens,
+                                                           int n_heads, int P, int64_t n_blocks) {
+  __shared__ __attribute__((aligned(16))) uint16_t WgP[M * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t WuP[M * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t WdP[D * HP];
+
+  const int64_t blk = xcd_remap(blockIdx.x, n_blocks);
+  const int head = (int)(blk / P);
+  const int chunk = (int)(blk % P);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int64_t C = (int64_t)n_heads * D;
+  const float* th = theta + (int64_t)head * PER_HEAD;
+
+  // A operand of G^T for k-step ks: lane (row hid, half hh) supplies
+  // W_g[e = 32hh + 8ks + j][hid]; stored at WgP[hid][16ks + 8hh + j].
+  for (int idx = tid; idx < M * D; idx += 256) {
+    const int hid = idx / D, kk = idx % D;
+    const int ks = kk >> 4, h2 = (kk >> 3) & 1, j = kk & 7;
+    const int e = 32 * h2 + 8 * ks + j;
+    WgP[hid * KP + kk] = f32_to_bf16_bits(th[e * M + hid]);
+    WuP[hid * KP + kk] = f32_to_bf16_bits(th[DM + e * M + hid]);
+  }
+  // A operand of Y^T for k-step s: lane (row o, half hh) supplies
+  // W_d[hid = 16s + 8(j/4) + 4hh + j%4][o] (the register order of H^T).
+  for (int idx = tid; idx < D * M; idx += 256) {
+    const int o = idx / M, kk = idx % M;
+    const int s = kk >> 4, h2 = (kk >> 3) & 1, j = kk & 7;
+    const int hid = 16 * s + 8 * (j >> 2) + 4 * h2 + (j & 3);
+    WdP[o * HP + kk] = f32_to_bf16_bits(th[2 * DM + hid * D + o]);
+  }
+  __syncthreads();
+
+  const int64_t n_tiles = (n_tokens + RT - 1) / RT;
+  const int64_t tile_begin = n_tiles * chunk / P;
+  const int64_t tile_end = n_tiles * (chunk + 1) / P;
+
+  for (int64_t tile = tile_begin + w; tile < tile_end; tile += 4) {
+    const int64_t t = tile * RT + l32;
+    const bool valid = t < n_tokens;
+    u32x4 qraw[4] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+    if (valid) {
+      const uint16_t* src = Q + t * C + (int64_t)head * D + 32 * hh;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qraw[ks] = ld16(src + 8 * ks);
+    }
+    bf16x8 q[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) q[ks] = as_bf16x8(qraw[ks]);
+    f32x16 accY[2] = {f32x16{}, f32x16{}};
+#pragma unroll 1
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x16 g = f32x16{}, u = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int off = (32 * mt + l32) * KP + 16 * ks + 8 * hh;
+        g = mfma32(ld_op(&WgP[off]), q[ks], g);
+        u = mfma32(ld_op(&WuP[off]), q[ks], u);
+      }
+      float h[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float s = sigmoid_fast(g[r]);
+        h[r] = g[r] * s * u[r];
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 hop = pack8(&h[8 * half]);
+        const int s = 2 * mt + half;
+#pragma unroll
+        for (int ot = 0; ot < 2; ++ot) {
+          accY[ot] = mfma32(ld_op(&WdP[(32 * ot + l32) * HP + 16 * s + 8 * hh]), hop, accY[ot]);
+        }
+      }
+    }
+    if (valid) {
+      uint16_t* dst = O + t * C + (int64_t)head * D;
+#pragma unroll
+      for (int ot = 0; ot < 2; ++ot) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          u32x2 v;
+          v[0] = pack_bf16x2(accY[ot][4 * q4 + 0], accY[ot][4 * q4 + 1]);
+          v[1] = pack_bf16x2(accY[ot][4 * q4 + 2], accY[ot][4 * q4 + 3]);
+          *reinterpret_cast<u32x2*>(dst + 32 * ot + 8 * q4 + 4 * hh) = v;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_read_bf16(const void* Q, const float* theta, void* O, int64_t n_tokens, int n_heads,
+                            hipStream_t stream) {
+  // Enough workgroups to fill 256 CUs twice over; each handles a contiguous
+  // run of 32-token tiles of one head.
+  const int64_t n_tiles = (n_tokens + RT - 1) / RT;
+  int64_t P = (512 + n_heads - 1) / n_heads;
+  if (P > n_tiles) P = n_tiles;
+  if (P < 1) P = 1;
+  const int64_t n_blocks = (int64_t)n_heads * P;
+  hipLaunchKernelGGL(read_bf16_kernel, dim3((unsigned)n_blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(Q), theta, static_cast<uint16_t*>(O), n_tokens, n_heads,
+                     (int)P, n_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace vggt3

@@ -45,3 +45,23 @@ def rel_err_per_head(x: np.ndarray, ref: np.ndarray, n_heads: int, axis_cols: bo
         return np.array([rel_err(x[h], ref[h]) for h in range(n_heads)])
     d = x.shape[1] // n_heads
     return np.array([rel_err(x[:, h * d:(h + 1) * d], ref[:, h * d:(h + 1) * d]) for h in range(n_heads)])
+
+
+def dtheta_ok(th: np.ndarray, th_ref: np.ndarray, th0: np.ndarray, n_heads: int, tol: float, steps: int):
+    """Per head: |(th - th0) - (th_ref - th0)| <= tol * max|th_ref - th0| + floor.
+
+    theta is stored in fp32 between steps, so each update theta - lr*g is
+    rounded to fp32: an absolute error of up to one fp32 ulp of |theta| per
+    step that no compute precision removes. floor = steps * 2^-23 * max|theta|.
+    Returns (ok, worst ratio of error to allowance).
+    """
+    th = th.reshape(n_heads, -1)
+    th_ref = th_ref.reshape(n_heads, -1)
+    th0 = th0.reshape(n_heads, -1)
+    worst = 0.0
+    for h in range(n_heads):
+        d, dr = th[h] - th0[h], th_ref[h] - th0[h]
+        floor = steps * 2.0 ** -23 * float(np.max(np.abs(th_ref[h])))
+        allow = tol * float(np.max(np.abs(dr))) + floor
+        worst = max(worst, float(np.max(np.abs(d - dr))) / allow)
+    return worst <= 1.0, worst

@@ -17,7 +17,7 @@ import torch
 import oracle
 import test_layer_amd as tla
 from synth import CONFIGS, make_inputs
-from tests.gpu_util import bits, f32_to_bits, rel_err, rel_err_per_head, to64
+from tests.gpu_util import bits, dtheta_ok, f32_to_bits, rel_err, rel_err_per_head, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -262,8 +262,12 @@ def test_tiny_f32_layer_parity():
     th_ref, L_ref, _ = oracle.ttt_write(to64(inp.K), Vp_ref.astype(np.float64), th0, 1, 16, 32, cfg.lr, cfg.steps)
     th = theta.cpu().numpy().astype(np.float64)
     assert rel_err(th, th_ref) <= TOL_F32
-    assert rel_err(th - th0, th_ref - th0) <= TOL_F32
+    ok, worst = dtheta_ok(th, th_ref, th0, 1, TOL_F32, cfg.steps)
+    assert ok, worst
     assert abs(loss.item() - L_ref[0, 0]) / L_ref[0, 0] <= TOL_F32
+    g = tla.ttt_grad(inp.K, Vp, inp.theta0, 1)
+    g_ref, _ = oracle.ttt_grad(to64(inp.K), Vp_ref.astype(np.float64), th0, 1, 16, 32)
+    assert rel_err(to64(g), g_ref) <= TOL_F32
     O_ref = oracle.ttt_read(to64(inp.Q), th_ref, 1, 16, 32)
     assert rel_err(to64(O), O_ref) <= TOL_F32
 
@@ -279,6 +283,11 @@ def test_f32_vggt_shape_parity():
     Vp_ref = _oracle_conv(inp, "f32").astype(np.float64)
     th_ref, _, _ = oracle.ttt_write(to64(inp.K), Vp_ref, th0, cfg.n_heads, 64, 128, cfg.lr, cfg.steps)
     th = theta.cpu().numpy().astype(np.float64)
-    assert rel_err_per_head(th - th0, th_ref - th0, cfg.n_heads, axis_cols=False).max() <= TOL_F32
+    assert rel_err_per_head(th, th_ref, cfg.n_heads, axis_cols=False).max() <= TOL_F32
+    ok, worst = dtheta_ok(th, th_ref, th0, cfg.n_heads, TOL_F32, cfg.steps)
+    assert ok, worst
+    g = tla.ttt_grad(inp.K, Vp, inp.theta0, cfg.n_heads)
+    g_ref, _ = oracle.ttt_grad(to64(inp.K), Vp_ref, th0, cfg.n_heads, 64, 128)
+    assert rel_err_per_head(to64(g), g_ref, cfg.n_heads, axis_cols=False).max() <= TOL_F32
     O_ref = oracle.ttt_read(to64(inp.Q), th_ref, cfg.n_heads, 64, 128)
     assert rel_err_per_head(to64(O), O_ref, cfg.n_heads).max() <= TOL_F32
