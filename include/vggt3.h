@@ -89,7 +89,8 @@ const char* vggt3_last_error(void);
  * Each patch output is evaluated in float32 as acc = +0; for a = -1..1 (outer),
  * b = -1..1 (inner): acc = fl(acc + fl(w*v)) — separately rounded, never fused;
  * then rounded to bf16 (ties to even) in bf16 mode. Special tokens are copied
- * bit for bit. channels must be a multiple of 8 (bf16) or 4 (f32).
+ * bit for bit. channels must be a multiple of 8 (bf16) or 4 (f32), and
+ * grid_w at most 4096.
  * n_views == 0 is a no-op.
  */
 int vggt3_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, int32_t grid_h,

@@ -139,6 +139,8 @@ int vggt3_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, in
     return fail(VGGT3_EUNSUPPORTED, "channels %d is not a multiple of %d", channels, vec);
   if ((int64_t)grid_h * grid_w > (1 << 24) || n_special > (1 << 20))
     return fail(VGGT3_EUNSUPPORTED, "view too large");
+  if (grid_w > vggt3::shortconv_max_grid_w())
+    return fail(VGGT3_EUNSUPPORTED, "grid_w %d exceeds %d", grid_w, vggt3::shortconv_max_grid_w());
   if (n_views == 0) return ok();
   if (V == nullptr || Vp == nullptr || w == nullptr) return fail(VGGT3_EINVAL, "NULL pointer");
   if (!aligned16(V) || !aligned16(Vp) || !aligned16(w)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");

@@ -23,6 +23,8 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t n) {
 constexpr int kMaxChunks = 64;
 int ttt_num_chunks(int64_t n_tokens, int n_heads, int tile_tokens);
 
+// Widest patch-grid row the ShortConv2D kernel stages in LDS.
+int shortconv_max_grid_w();
 hipError_t launch_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, int grid_h,
                             int grid_w, int n_special, int C, bool bf16, hipStream_t stream);
 

@@ -6,13 +6,16 @@
 // flattened again; per its Appendix A note, camera and register tokens bypass
 // the conv. The conv is depthwise (one 3x3 filter per channel), zero padded.
 //
-// Design (HBM-bound stencil): one thread owns one (view, column x, 16-byte
-// channel group) and walks down the column keeping a 3x3 window of fp32
-// vectors in registers, so each input row is loaded once per thread and the
-// x-1 / x+1 loads of neighbouring threads hit L1/L2. Lanes of a wave cover
-// consecutive channel groups of one token, so every load and store is a
-// contiguous 1 KB wave transaction. Workgroups are remapped so that each XCD
-// walks a contiguous range of columns (the x+-1 re-reads stay in its L2).
+// Design (HBM-bound stencil). One thread owns one (view, column x, segment of
+// SEG rows, 4-channel group). It issues the loads of all SEG+2 input rows of
+// its segment at columns x-1, x, x+1 at once (8 bytes each; about 18 KB in
+// flight per wave, which is what keeps HBM busy), then computes the SEG output
+// rows with a rotating 3x3 window of fp32 vectors in registers. The code is
+// straight-line: rows outside the grid load as zero and only the stores of
+// rows past the segment are skipped. Lanes of a wave cover consecutive channel
+// groups of one token (512 contiguous bytes per wave access); the x-1 / x+1
+// re-reads of neighbouring columns hit L1/L2, and workgroups are remapped so
+// that each XCD walks a contiguous range of columns.
 //
 // Bit-exact contract: acc = +0; taps with the row offset outermost and the
 // column offset innermost; acc = fl(acc + fl(w*v)), never fused (this file is
@@ -26,143 +29,172 @@
 
 namespace vggt3 {
 
+namespace {
+
+constexpr int SEG = 10;     // output rows per thread (37 rows -> 4 segments)
+constexpr int MAX_W = 4096;  // widest grid row accepted (no staging limit in this design)
+
 template <bool BF16>
 struct ConvTraits;
 template <>
 struct ConvTraits<true> {
-  static constexpr int VEC = 8;  // 8 bf16 = 16 bytes
-  __device__ static void load(const void* base, int64_t elem, float (&v)[8]) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_lo(q[i]);
-      v[2 * i + 1] = bf16_hi(q[i]);
-    }
+  static constexpr int ESZ = 2;
+  typedef u32x2 vec_t;  // 4 bf16
+  __device__ static void widen(const vec_t& q, float (&v)[4]) {
+    v[0] = bf16_lo(q[0]);
+    v[1] = bf16_hi(q[0]);
+    v[2] = bf16_lo(q[1]);
+    v[3] = bf16_hi(q[1]);
   }
-  __device__ static void store(void* base, int64_t elem, const float (&v)[8]) {
-    u32x4 q;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(base) + elem) = q;
-  }
-  __device__ static void copy(const void* src, void* dst, int64_t elem) {
-    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(dst) + elem) =
-        *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(src) + elem);
+  __device__ static vec_t narrow(const float (&v)[4]) {
+    return vec_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   }
 };
 template <>
 struct ConvTraits<false> {
-  static constexpr int VEC = 4;  // 4 fp32 = 16 bytes
-  __device__ static void load(const void* base, int64_t elem, float (&v)[4]) {
-    const f32x4 q = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + elem);
+  static constexpr int ESZ = 4;
+  typedef u32x4 vec_t;  // 4 fp32
+  __device__ static void widen(const vec_t& q, float (&v)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = q[i];
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(q[i]);
   }
-  __device__ static void store(void* base, int64_t elem, const float (&v)[4]) {
-    f32x4 q;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = v[i];
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + elem) = q;
-  }
-  __device__ static void copy(const void* src, void* dst, int64_t elem) {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dst) + elem) =
-        *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(src) + elem);
+  __device__ static vec_t narrow(const float (&v)[4]) {
+    return vec_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
   }
 };
 
-template <bool BF16>
-__global__ __launch_bounds__(256) void shortconv_kernel(const void* __restrict__ V, void* __restrict__ Vp,
-                                                         const float* __restrict__ w, int64_t n_items,
-                                                         int grid_h, int grid_w, int n_special, int C,
-                                                         int64_t n_blocks) {
-  using Tr = ConvTraits<BF16>;
-  constexpr int VEC = Tr::VEC;
-  const int64_t blk = xcd_remap(blockIdx.x, n_blocks);
-  const int64_t item = blk * 256 + threadIdx.x;
-  if (item >= n_items) return;
-  const int CG = C / VEC;
-  const int cg = (int)(item % CG);
-  const int64_t vx = item / CG;
-  const int x = (int)(vx % grid_w);
-  const int64_t view = vx / grid_w;
-  const int c0 = cg * VEC;
-  const int64_t tpv = (int64_t)n_special + (int64_t)grid_h * grid_w;
-  const int64_t view_base = view * tpv;  // first token of the view
-
-  if (x == 0) {
-    for (int s = 0; s < n_special; ++s) Tr::copy(V, Vp, (view_base + s) * C + c0);
-  }
-
-  // Filter taps for this thread's channels: wt[tap][ch], tap = (a+1)*3 + (b+1).
-  float wt[9][VEC];
+// One output row: acc = sum over taps, row offset outermost, column innermost.
+__device__ __forceinline__ void conv_row(const float (&wt)[9][4], const float (&up)[3][4],
+                                         const float (&mid)[3][4], const float (&dn)[3][4], float (&acc)[4]) {
 #pragma unroll
-  for (int ch = 0; ch < VEC; ++ch) {
-#pragma unroll
-    for (int t = 0; t < 9; ++t) wt[t][ch] = w[(int64_t)(c0 + ch) * 9 + t];
-  }
-
-  const int64_t patch_base = view_base + n_special;
-  // Window rows: win[0] = row y-1, win[1] = row y, win[2] = row y+1; columns x-1, x, x+1.
-  float win[3][3][VEC];
+  for (int ch = 0; ch < 4; ++ch) acc[ch] = 0.0f;
 #pragma unroll
   for (int b = 0; b < 3; ++b)
 #pragma unroll
-    for (int ch = 0; ch < VEC; ++ch) win[0][b][ch] = 0.0f;
+    for (int ch = 0; ch < 4; ++ch) acc[ch] = acc[ch] + wt[b][ch] * up[b][ch];
+#pragma unroll
+  for (int b = 0; b < 3; ++b)
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) acc[ch] = acc[ch] + wt[3 + b][ch] * mid[b][ch];
+#pragma unroll
+  for (int b = 0; b < 3; ++b)
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) acc[ch] = acc[ch] + wt[6 + b][ch] * dn[b][ch];
+}
 
-  auto load_row = [&](int y, float (&row)[3][VEC]) {
+template <bool BF16>
+__global__ __launch_bounds__(256) void shortconv_kernel(const char* __restrict__ V, char* __restrict__ Vp,
+                                                         const float* __restrict__ w, int64_t n_items,
+                                                         int grid_h, int grid_w, int n_special, int C,
+                                                         int n_seg, int64_t n_blocks) {
+  using Tr = ConvTraits<BF16>;
+  typedef typename Tr::vec_t vec_t;
+  constexpr int VB = (int)sizeof(vec_t);  // bytes per 4-channel group
+  const int64_t blk = xcd_remap(blockIdx.x, n_blocks);
+  const int64_t item = blk * 256 + threadIdx.x;
+  if (item >= n_items) return;
+  // item -> (view, column x, segment, channel group); channel group fastest.
+  const int CG = C / 4;
+  const int cg = (int)(item % CG);
+  int64_t rest = item / CG;
+  const int seg = (int)(rest % n_seg);
+  rest /= n_seg;
+  const int x = (int)(rest % grid_w);
+  const int64_t view = rest / grid_w;
+  const int64_t row_bytes = (int64_t)C * Tr::ESZ;
+  const int64_t tpv = (int64_t)n_special + (int64_t)grid_h * grid_w;
+  const char* vview = V + view * tpv * row_bytes + (int64_t)cg * VB;
+  char* oview = Vp + view * tpv * row_bytes + (int64_t)cg * VB;
+
+  if (x == 0 && seg == 0) {
+    for (int s = 0; s < n_special; ++s)
+      *reinterpret_cast<vec_t*>(oview + s * row_bytes) = *reinterpret_cast<const vec_t*>(vview + s * row_bytes);
+  }
+
+  const int y0 = seg * SEG;
+  const int64_t grid_row = (int64_t)grid_w * row_bytes;  // bytes from one grid row to the next
+  const char* src = vview + (int64_t)n_special * row_bytes + (int64_t)x * row_bytes;  // (y = 0, x)
+  char* dst = oview + (int64_t)n_special * row_bytes + (int64_t)x * row_bytes;
+  const bool has_l = x > 0, has_r = x + 1 < grid_w;
+
+  // Loads of input rows y0-1 .. y0+SEG at columns x-1, x, x+1. Every load is
+  // issued (from a clamped, in-grid address) and taps outside the grid are
+  // then replaced by zero with a select: with no conditional loads the
+  // compiler's load-counter waits stay exact, so all 36 loads stay in flight.
+  const int xl = has_l ? -1 : 0, xr = has_r ? 1 : 0;
+  vec_t raw[SEG + 2][3];
 #pragma unroll
-    for (int b = 0; b < 3; ++b) {
-      const int xx = x + b - 1;
-      if (y < grid_h && xx >= 0 && xx < grid_w) {
-        Tr::load(V, (patch_base + (int64_t)y * grid_w + xx) * C + c0, row[b]);
-      } else {
+  for (int k = 0; k < SEG + 2; ++k) {
+    const int y = y0 - 1 + k;
+    const int yc = y < 0 ? 0 : (y >= grid_h ? grid_h - 1 : y);
+    const char* p = src + (int64_t)yc * grid_row;
+    raw[k][0] = *reinterpret_cast<const vec_t*>(p + xl * row_bytes);
+    raw[k][1] = *reinterpret_cast<const vec_t*>(p);
+    raw[k][2] = *reinterpret_cast<const vec_t*>(p + xr * row_bytes);
+  }
 #pragma unroll
-        for (int ch = 0; ch < VEC; ++ch) row[b][ch] = 0.0f;
-      }
-    }
+  for (int k = 0; k < SEG + 2; ++k) {
+    const int y = y0 - 1 + k;
+    const bool in = y >= 0 && y < grid_h;
+    if (!(in && has_l)) raw[k][0] = vec_t{};
+    if (!in) raw[k][1] = vec_t{};
+    if (!(in && has_r)) raw[k][2] = vec_t{};
+  }
+
+  float wt[9][4];
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+    for (int t = 0; t < 9; ++t) wt[t][ch] = w[(int64_t)(cg * 4 + ch) * 9 + t];
+
+  float rA[3][4], rB[3][4], rC[3][4], acc[4];
+  auto widen_row = [&](int k, float (&row)[3][4]) {
+#pragma unroll
+    for (int b = 0; b < 3; ++b) Tr::widen(raw[k][b], row[b]);
   };
-
-  load_row(0, win[1]);
-  for (int y = 0; y < grid_h; ++y) {
-    load_row(y + 1, win[2]);
-    float acc[VEC];
+  auto store_row = [&](int k) {
+    const int y = y0 + k;
+    if (y < grid_h) *reinterpret_cast<vec_t*>(dst + (int64_t)y * grid_row) = Tr::narrow(acc);
+  };
+  widen_row(0, rA);
+  widen_row(1, rB);
 #pragma unroll
-    for (int ch = 0; ch < VEC; ++ch) acc[ch] = 0.0f;
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-#pragma unroll
-      for (int b = 0; b < 3; ++b) {
-#pragma unroll
-        for (int ch = 0; ch < VEC; ++ch) {
-          const float p = wt[a * 3 + b][ch] * win[a][b][ch];
-          acc[ch] = acc[ch] + p;
-        }
-      }
+  for (int k = 0; k < SEG; k += 3) {
+    widen_row(k + 2, rC);
+    conv_row(wt, rA, rB, rC, acc);
+    store_row(k);
+    if (k + 1 < SEG) {
+      widen_row(k + 3, rA);
+      conv_row(wt, rB, rC, rA, acc);
+      store_row(k + 1);
     }
-    Tr::store(Vp, (patch_base + (int64_t)y * grid_w + x) * C + c0, acc);
-#pragma unroll
-    for (int b = 0; b < 3; ++b)
-#pragma unroll
-      for (int ch = 0; ch < VEC; ++ch) {
-        win[0][b][ch] = win[1][b][ch];
-        win[1][b][ch] = win[2][b][ch];
-      }
+    if (k + 2 < SEG) {
+      widen_row(k + 4, rB);
+      conv_row(wt, rC, rA, rB, acc);
+      store_row(k + 2);
+    }
   }
 }
 
+}  // namespace
+
 hipError_t launch_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, int grid_h,
                             int grid_w, int n_special, int C, bool bf16, hipStream_t stream) {
-  const int VEC = bf16 ? 8 : 4;
-  const int64_t n_items = n_views * grid_w * (int64_t)(C / VEC);
+  const int n_seg = (grid_h + SEG - 1) / SEG;
+  const int64_t n_items = n_views * grid_w * (int64_t)n_seg * (C / 4);
   if (n_items == 0) return hipSuccess;
   const int64_t n_blocks = (n_items + 255) / 256;
   if (bf16)
-    hipLaunchKernelGGL(shortconv_kernel<true>, dim3((unsigned)n_blocks), dim3(256), 0, stream, V, Vp, w,
-                       n_items, grid_h, grid_w, n_special, C, n_blocks);
+    hipLaunchKernelGGL(shortconv_kernel<true>, dim3((unsigned)n_blocks), dim3(256), 0, stream,
+                       static_cast<const char*>(V), static_cast<char*>(Vp), w, n_items, grid_h, grid_w,
+                       n_special, C, n_seg, n_blocks);
   else
-    hipLaunchKernelGGL(shortconv_kernel<false>, dim3((unsigned)n_blocks), dim3(256), 0, stream, V, Vp, w,
-                       n_items, grid_h, grid_w, n_special, C, n_blocks);
+    hipLaunchKernelGGL(shortconv_kernel<false>, dim3((unsigned)n_blocks), dim3(256), 0, stream,
+                       static_cast<const char*>(V), static_cast<char*>(Vp), w, n_items, grid_h, grid_w,
+                       n_special, C, n_seg, n_blocks);
   return hipGetLastError();
 }
+
+int shortconv_max_grid_w() { return MAX_W; }
 
 }  // namespace vggt3

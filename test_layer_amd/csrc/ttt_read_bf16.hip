@@ -25,8 +25,9 @@ constexpr int PER_HEAD = 3 * DM;
 // Each wave handles 32 tokens per iteration.
 // ---------------------------------------------------------------------------
 constexpr int RT = 32;  // tokens per wave iteration
+constexpr int NW = 8;   // waves per workgroup
 
-__global__ __launch_bounds__(256, 2) void read_bf16_kernel(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(512, 2) void read_bf16_kernel(const uint16_t* __restrict__ Q,
                                                            const float* __restrict__ theta,
                                                            uint16_t* __restrict__ O, int64_t n_tokens,
                                                            int n_heads, int P, int64_t n_blocks) {
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(256, 2) void read_bf16_kernel(const uint16_t* __res
 
   // A operand of G^T for k-step ks: lane (row hid, half hh) supplies
   // W_g[e = 32hh + 8ks + j][hid]; stored at WgP[hid][16ks + 8hh + j].
-  for (int idx = tid; idx < M * D; idx += 256) {
+  for (int idx = tid; idx < M * D; idx += 64 * NW) {
     const int hid = idx / D, kk = idx % D;
     const int ks = kk >> 4, h2 = (kk >> 3) & 1, j = kk & 7;
     const int e = 32 * h2 + 8 * ks + j;
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(256, 2) void read_bf16_kernel(const uint16_t* __res
   }
   // A operand of Y^T for k-step s: lane (row o, half hh) supplies
   // W_d[hid = 16s + 8(j/4) + 4hh + j%4][o] (the register order of H^T).
-  for (int idx = tid; idx < D * M; idx += 256) {
+  for (int idx = tid; idx < D * M; idx += 64 * NW) {
     const int o = idx / M, kk = idx % M;
     const int s = kk >> 4, h2 = (kk >> 3) & 1, j = kk & 7;
     const int hid = 16 * s + 8 * (j >> 2) + 4 * h2 + (j & 3);
@@ -68,25 +69,37 @@ __global__ __launch_bounds__(256, 2) void read_bf16_kernel(const uint16_t* __res
   const int64_t tile_begin = n_tiles * chunk / P;
   const int64_t tile_end = n_tiles * (chunk + 1) / P;
 
-  for (int64_t tile = tile_begin + w; tile < tile_end; tile += 4) {
+  // Each wave walks tiles tile_begin + w, + NW, ...; the next tile's queries
+  // are loaded while the current one computes.
+  // Loads are unconditional (rows past the end read the last token and are
+  // never stored), so the compiler's load-counter waits stay exact.
+  auto load_q = [&](int64_t tile, u32x4 (&dst)[4]) {
+    int64_t t = tile * RT + l32;
+    t = t < n_tokens ? t : n_tokens - 1;
+    const uint16_t* src = Q + t * C + (int64_t)head * D + 32 * hh;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) dst[ks] = ld16(src + 8 * ks);
+  };
+  // Two query register sets alternate (no loop-carried copies, so the load
+  // waits stay exact): tile k computes from one set while tile k+1 loads into
+  // the other.
+  auto compute_tile = [&](int64_t tile, const u32x4 (&qr)[4]) {
     const int64_t t = tile * RT + l32;
     const bool valid = t < n_tokens;
-    u32x4 qraw[4] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
-    if (valid) {
-      const uint16_t* src = Q + t * C + (int64_t)head * D + 32 * hh;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qraw[ks] = ld16(src + 8 * ks);
-    }
     bf16x8 q[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) q[ks] = as_bf16x8(qraw[ks]);
+    for (int ks = 0; ks < 4; ++ks) q[ks] = as_bf16x8(qr[ks]);
+    // The weight reads below are loop-invariant; an opaque zero offset keeps the
+    // compiler from hoisting 48 operand vectors into registers (and spilling).
+    int lds0 = 0;
+    asm volatile("" : "+v"(lds0));
     f32x16 accY[2] = {f32x16{}, f32x16{}};
-#pragma unroll 1
+#pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       f32x16 g = f32x16{}, u = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int off = (32 * mt + l32) * KP + 16 * ks + 8 * hh;
+        const int off = lds0 + (32 * mt + l32) * KP + 16 * ks + 8 * hh;
         g = mfma32(ld_op(&WgP[off]), q[ks], g);
         u = mfma32(ld_op(&WuP[off]), q[ks], u);
       }
@@ -102,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void read_bf16_kernel(const uint16_t* __res
         const int s = 2 * mt + half;
 #pragma unroll
         for (int ot = 0; ot < 2; ++ot) {
-          accY[ot] = mfma32(ld_op(&WdP[(32 * ot + l32) * HP + 16 * s + 8 * hh]), hop, accY[ot]);
+          accY[ot] = mfma32(ld_op(&WdP[lds0 + (32 * ot + l32) * HP + 16 * s + 8 * hh]), hop, accY[ot]);
         }
       }
     }
@@ -119,6 +132,14 @@ __global__ __launch_bounds__(256, 2) void read_bf16_kernel(const uint16_t* __res
         }
       }
     }
+  };
+  u32x4 qa[4], qb[4];
+  load_q(tile_begin + w, qa);
+  for (int64_t tile = tile_begin + w; tile < tile_end; tile += 2 * NW) {
+    load_q(tile + NW, qb);
+    compute_tile(tile, qa);
+    load_q(tile + 2 * NW, qa);
+    if (tile + NW < tile_end) compute_tile(tile + NW, qb);
   }
 }
 
@@ -133,7 +154,7 @@ hipError_t launch_read_bf16(const void* Q, const float* theta, void* O, int64_t 
   if (P > n_tiles) P = n_tiles;
   if (P < 1) P = 1;
   const int64_t n_blocks = (int64_t)n_heads * P;
-  hipLaunchKernelGGL(read_bf16_kernel, dim3((unsigned)n_blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL(read_bf16_kernel, dim3((unsigned)n_blocks), dim3(64 * NW), 0, stream,
                      static_cast<const uint16_t*>(Q), theta, static_cast<uint16_t*>(O), n_tokens, n_heads,
                      (int)P, n_blocks);
   return hipGetLastError();

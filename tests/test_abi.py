@@ -74,6 +74,7 @@ def test_shortconv_validation(lib):
     assert call(gh=0) == tla.EINVAL
     assert call(ns=-1) == tla.EINVAL
     assert call(C=12) == tla.EUNSUPPORTED  # not a multiple of 8 in bf16
+    assert call(gw=5000) == tla.EUNSUPPORTED  # wider than the kernel accepts
     assert call(V=None) == tla.EINVAL
     assert call(V=ctypes.c_void_p(0x10008)) == tla.EINVAL  # misaligned
     assert call(Vp=FAKE) == tla.EINVAL and "overlap" in _err(lib)  # in place
