@@ -24,9 +24,13 @@ __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
-// Two fp32 -> packed bf16 pair (lo = a, hi = b), round to nearest even.
+// Two fp32 -> packed bf16 pair (lo = a, hi = b), round to nearest even, as one
+// v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // 32x32x16 bf16 MFMA, fp32 accumulate.

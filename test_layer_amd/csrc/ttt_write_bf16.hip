@@ -26,16 +26,27 @@
 //
 // Workgroup = 4 waves; wave w owns hidden units [32w, 32w+32): G, U, H, dH,
 // dG, dU for those units and the matching gradient slices gW_g[:, w-slice],
-// gW_u[:, w-slice], gW_d[w-slice, :] (96 fp32 accumulators per lane, kept in
-// registers for the whole chunk). Per 64-token tile c the workgroup runs
+// gW_u[:, w-slice], gW_d[w-slice, :] (96 fp32 accumulators per lane, kept for
+// the whole chunk). W_g / W_u operands live in registers, W_d in LDS. Per
+// 64-token tile c the workgroup runs
 //   B0 | G,U(c) ; gradients(c-1) ; SwiGLU(c) -> H ; stage K,V'(c+1)
 //   B1 | Y(c) = H W_d ; R, loss ; Y -> LDS
 //   B2 | dH(c) = (Y - V') W_d^T ; dG, dU
 // so the gradient MFMAs of one tile overlap the SwiGLU VALU work of the next.
 // K and V' tiles rotate through 3 LDS buffers and Y through 2; global loads of
-// tile c+2 are issued while tile c computes.
+// tile c+2 are issued while tile c computes. All LDS addressing is 32-bit.
 #include "bf16_ops.hpp"
 #include "kernels.hpp"
+
+#ifndef VGGT3_WRITE_TP
+#define VGGT3_WRITE_TP 72
+#endif
+#ifndef VGGT3_WRITE_HP
+#define VGGT3_WRITE_HP 72
+#endif
+#ifndef VGGT3_WRITE_WP
+#define VGGT3_WRITE_WP 72
+#endif
 
 namespace vggt3 {
 namespace {
@@ -45,24 +56,49 @@ constexpr int M = 128;     // hidden units
 constexpr int T = 64;      // tokens per tile
 constexpr int DM = D * M;
 constexpr int PER_HEAD = 3 * DM;
-constexpr int TP = 72;     // LDS pitch (elements) of [64][64] tiles: K[t][e], Vn[t][o], Y[o][t]
-constexpr int HPT = 72;    // LDS pitch of H[hid][t]
+constexpr int TP = VGGT3_WRITE_TP;   // pitch (elements) of [64][64] tiles: K[t][e], Vn[t][o], Y[o][t]
+constexpr int HPT = VGGT3_WRITE_HP;  // pitch of H[hid][t]
+constexpr int WP = VGGT3_WRITE_WP;   // pitch of W_d[hid][o]
 constexpr int KV_BUFS = 3;
 constexpr int Y_BUFS = 2;
+constexpr int TSZ = T * TP;          // elements per token tile
 
-struct Smem {
-  uint16_t K[KV_BUFS][T * TP];
-  uint16_t Vn[KV_BUFS][T * TP];  // -V'
-  uint16_t Y[Y_BUFS][D * TP];    // [o][t]
-  uint16_t H[M * HPT];           // [hid][t]
-  float red[4];
-};
+// LDS map (elements of bf16).
+constexpr int OFF_K = 0;
+constexpr int OFF_V = OFF_K + KV_BUFS * TSZ;
+constexpr int OFF_Y = OFF_V + KV_BUFS * TSZ;
+constexpr int OFF_H = OFF_Y + Y_BUFS * TSZ;
+constexpr int OFF_W = OFF_H + M * HPT;
+constexpr int LDS_ELEMS = OFF_W + M * WP;
+
+typedef __attribute__((address_space(3))) uint16_t lu16;
+typedef __attribute__((address_space(3))) u32x4 lu32x4;
+typedef __attribute__((address_space(3))) u32x2 lu32x2;
+
+__device__ __forceinline__ u32x4 lld16(const lu16* p) { return *(const lu32x4*)p; }
+__device__ __forceinline__ u32x2 lld8(const lu16* p) { return *(const lu32x2*)p; }
+__device__ __forceinline__ void lst16(lu16* p, const u32x4& v) { *(lu32x4*)p = v; }
+__device__ __forceinline__ void lst8(lu16* p, const u32x2& v) { *(lu32x2*)p = v; }
+__device__ __forceinline__ u32x2 ltr(const lu16* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+}
+__device__ __forceinline__ bf16x8 lop(const lu16* p) { return as_bf16x8(lld16(p)); }
+__device__ __forceinline__ bf16x8 ltr_op(const lu16* p0, const lu16* p1) {
+  const u32x2 a = ltr(p0), b = ltr(p1);
+  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+}
+__device__ __forceinline__ bf16x8 lpair_op(const lu16* p0, const lu16* p1) {
+  const u32x2 a = lld8(p0), b = lld8(p1);
+  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+}
 
 __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
     const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg, const float* __restrict__ theta,
     float* __restrict__ part, float* __restrict__ loss_part, int64_t n_tokens, int n_heads, int P,
     int64_t n_blocks) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[LDS_ELEMS];
+  __shared__ float red[4];
+  lu16* const lds = (lu16*)smem;
 
   const int64_t blk = xcd_remap(blockIdx.x, n_blocks);
   const int head = (int)(blk / P);
@@ -83,34 +119,28 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
   const float* Wu = th + DM;
   const float* Wd = th + 2 * DM;
 
-  // Weight operands (bf16, round to nearest even) held in registers.
-  //   WgB/WuB[ks]: B[k = e][j = hid], e = 16ks + 8hh + jj, hid = 32w + l32   (G, U)
-  //   WdB[ks]:     B[k = hid][j = o], hid = 16ks + 8hh + jj, o = 32ob + l32  (Y)
-  //   WdTB[ks]:    B[k = o][j = hid], o = 16ks + 8hh + jj, hid = 32w + l32   (dH)
-  bf16x8 WgB[4], WuB[4], WdB[8], WdTB[4];
+  // W_g / W_u operands in registers: B[k = e][j = hid], e = 16ks + 8hh + jj, hid = 32w + l32.
+  bf16x8 WgB[4], WuB[4];
   {
     const int hid = 32 * w + l32;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      float g[8], u[8], dt[8];
+      float g[8], u[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int e = 16 * ks + 8 * hh + j;
         g[j] = Wg[e * M + hid];
         u[j] = Wu[e * M + hid];
-        dt[j] = Wd[hid * D + e];
       }
       WgB[ks] = pack8(g);
       WuB[ks] = pack8(u);
-      WdTB[ks] = pack8(dt);
     }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      float v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = Wd[(16 * ks + 8 * hh + j) * D + 32 * ob + l32];
-      WdB[ks] = pack8(v);
-    }
+  }
+  // W_d (bf16) in LDS, natural [hid][o] layout.
+  for (int idx = tid; idx < M * D / 2; idx += 256) {
+    const int hid = (2 * idx) / D, o = (2 * idx) % D;
+    *(__attribute__((address_space(3))) uint32_t*)(lds + OFF_W + hid * WP + o) =
+        pack_bf16x2(Wd[hid * D + o], Wd[hid * D + o + 1]);
   }
 
   f32x16 accWd[2], accWg[2], accWu[2];
@@ -126,8 +156,22 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
   const int64_t tile_begin = n_tiles_all * chunk / P;
   const int nt = (int)(n_tiles_all * (chunk + 1) / P - tile_begin);
 
+  // Lane-constant LDS offsets (elements).
+  const int o_row = l32 * TP + 8 * hh;                    // row-major operand rows (b128)
+  const int o_tr = (4 * hh + jr) * TP + cb + 4 * q4;       // transpose reads over token rows
+  const int o_htr = (8 * hh + jr) * HPT + cb + 4 * q4;     // transpose reads of H[hid][t]
+  const int o_ytr = (8 * hh + jr) * TP + cb + 4 * q4;      // transpose reads of Y[o][t]
+  const int o_wtr = (8 * hh + jr) * WP + cb + 4 * q4;      // transpose reads of W_d[hid][o]
+  const int o_wrow = (32 * w + l32) * WP + 8 * hh;         // W_d rows of this wave's units
+  const int o_yrow = l32 * TP + 4 * hh;                    // Y[o][t] runs for gW_d
+  const int o_hst = (32 * w + l32) * HPT + 4 * hh;         // H stores
+  const int o_yst = (32 * ob + l32) * TP + 32 * tb + 4 * hh;  // Y stores
+
   // Tile staging: thread -> rows (tid>>3) and (tid>>3)+32, 8 channels at (tid&7)*8.
+  // Loads are unconditional (rows past the end re-read the last token and are
+  // zeroed), which keeps the compiler's load-counter waits exact.
   const int srow = tid >> 3, scol = (tid & 7) * 8;
+  const int o_stage = srow * TP + scol;
   const uint16_t* Kh = Kg + (int64_t)head * D + scol;
   const uint16_t* Vh = Vg + (int64_t)head * D + scol;
   u32x4 kr[2], vr[2];
@@ -135,29 +179,29 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
     const int64_t tok0 = (tile_begin + i) * T;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int64_t tok = tok0 + srow + 32 * s;
-      kr[s] = u32x4{0u, 0u, 0u, 0u};
-      vr[s] = u32x4{0u, 0u, 0u, 0u};
-      if (tok < n_tokens) {
-        kr[s] = ld16(Kh + tok * C);
-        vr[s] = ld16(Vh + tok * C);
-      }
+      int64_t tok = tok0 + srow + 32 * s;
+      tok = tok < n_tokens ? tok : n_tokens - 1;
+      kr[s] = ld16(Kh + tok * C);
+      vr[s] = ld16(Vh + tok * C);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int i) {
+    const int buf = i % KV_BUFS;
+    const int64_t tok0 = (tile_begin + i) * T;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int r = srow + 32 * s;
-      st16(&sm.K[buf][r * TP + scol], kr[s]);
-      st16(&sm.Vn[buf][r * TP + scol], vr[s] ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u});
+      const bool ok = tok0 + srow + 32 * s < n_tokens;
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+      lst16(lds + OFF_K + buf * TSZ + o_stage + 32 * s * TP, ok ? kr[s] : z);
+      lst16(lds + OFF_V + buf * TSZ + o_stage + 32 * s * TP,
+            ok ? (vr[s] ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}) : z);
     }
   };
 
   // Operands of the previous tile's gradient contractions (k-slot jj of k-step
   // ks is token 16ks + 8(jj/4) + 4hh + jj%4, the register order of C tiles).
-  // They start at zero, with zeroed "tile -1" buffers, so that the gradient
-  // step can run unconditionally inside the loop body (one basic block for the
-  // MFMA / VALU overlap) and contributes nothing on the first iteration.
+  // They start at zero, with zeroed "tile -1" buffers, so the gradient step
+  // runs unconditionally inside the loop body and adds nothing the first time.
   bf16x8 Hop[4], dGop[4], dUop[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -165,32 +209,31 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
     dGop[ks] = Hop[ks];
     dUop[ks] = Hop[ks];
   }
-  for (int idx = tid * 8; idx < T * TP; idx += 256 * 8) {
-    st16(&sm.K[KV_BUFS - 1][idx], u32x4{0u, 0u, 0u, 0u});
-    st16(&sm.Vn[KV_BUFS - 1][idx], u32x4{0u, 0u, 0u, 0u});
-    st16(&sm.Y[Y_BUFS - 1][idx], u32x4{0u, 0u, 0u, 0u});
+  for (int idx = tid * 8; idx < TSZ; idx += 256 * 8) {
+    lst16(lds + OFF_K + (KV_BUFS - 1) * TSZ + idx, u32x4{0u, 0u, 0u, 0u});
+    lst16(lds + OFF_V + (KV_BUFS - 1) * TSZ + idx, u32x4{0u, 0u, 0u, 0u});
+    lst16(lds + OFF_Y + (Y_BUFS - 1) * TSZ + idx, u32x4{0u, 0u, 0u, 0u});
   }
 
   auto gradients = [&](int kvb, int yb) {
-    const uint16_t* Kp = sm.K[kvb];
-    const uint16_t* Vp = sm.Vn[kvb];
-    const uint16_t* Yp = sm.Y[yb];
+    const lu16* Kp = lds + OFF_K + kvb * TSZ;
+    const lu16* Vp = lds + OFF_V + kvb * TSZ;
+    const lu16* Yp = lds + OFF_Y + yb * TSZ;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int r0 = 16 * ks + 4 * hh + jr;  // transpose-read source rows (tokens)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const int o = 32 * nb + l32;
-        const bf16x8 yB = pair_op(&Yp[o * TP + 16 * ks + 4 * hh], &Yp[o * TP + 16 * ks + 8 + 4 * hh]);
-        const int oc = 32 * nb + cb + 4 * q4;
-        const bf16x8 vB = tr_op(&Vp[r0 * TP + oc], &Vp[(r0 + 8) * TP + oc]);
+        const lu16* yr = Yp + o_yrow + 32 * nb * TP + 16 * ks;
+        const bf16x8 yB = lpair_op(yr, yr + 8);
+        const lu16* vt = Vp + o_tr + 16 * ks * TP + 32 * nb;
+        const bf16x8 vB = ltr_op(vt, vt + 8 * TP);
         accWd[nb] = mfma32(Hop[ks], yB, accWd[nb]);
         accWd[nb] = mfma32(Hop[ks], vB, accWd[nb]);
       }
 #pragma unroll
       for (int eb = 0; eb < 2; ++eb) {
-        const int ec = 32 * eb + cb + 4 * q4;
-        const bf16x8 kA = tr_op(&Kp[r0 * TP + ec], &Kp[(r0 + 8) * TP + ec]);
+        const lu16* kt = Kp + o_tr + 16 * ks * TP + 32 * eb;
+        const bf16x8 kA = ltr_op(kt, kt + 8 * TP);
         accWg[eb] = mfma32(kA, dGop[ks], accWg[eb]);
         accWu[eb] = mfma32(kA, dUop[ks], accWu[eb]);
       }
@@ -206,8 +249,9 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
   for (int i = 0; i < nt; ++i) {
     const int kvb = i % KV_BUFS;
     const int yb = i & 1;
-    const uint16_t* Kc = sm.K[kvb];
-    const uint16_t* Vc = sm.Vn[kvb];
+    const lu16* Kc = lds + OFF_K + kvb * TSZ;
+    const lu16* Vc = lds + OFF_V + kvb * TSZ;
+    lu16* Yc = lds + OFF_Y + yb * TSZ;
     __syncthreads();  // B0: K, V'(i) staged; everything of tile i-2 consumed
 
     // G, U of tile i: element (mt, r) is token 32mt + 8(r/4) + 4hh + r%4, unit 32w + l32.
@@ -218,7 +262,7 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
       accU[mt] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = ld_op(&Kc[(32 * mt + l32) * TP + 16 * ks + 8 * hh]);
+        const bf16x8 a = lop(Kc + o_row + 32 * mt * TP + 16 * ks);
         accG[mt] = mfma32(a, WgB[ks], accG[mt]);
         accU[mt] = mfma32(a, WuB[ks], accU[mt]);
       }
@@ -227,36 +271,40 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
     gradients((i + KV_BUFS - 1) % KV_BUFS, (i + 1) & 1);  // tile i-1
 
     // SwiGLU: s = sigmoid(G), A = G s, H = A U, gp = U silu'(G) = U s + H (1 - s).
-    float Af[2][16], GP[2][16], Hf[2][16];
+    // A and gp are kept as bf16 pairs until the backward step.
+    uint32_t Ap[2][8], GPp[2][8];
+    float Hf[2][16];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float g = accG[mt][r];
-        const float u = accU[mt][r];
-        const float s = sigmoid_fast(g);
-        const float a = g * s;
-        const float h = a * u;
-        Af[mt][r] = a;
-        Hf[mt][r] = h;
-        GP[mt][r] = fmaf(-h, s, fmaf(u, s, h));
+      for (int r = 0; r < 16; r += 2) {
+        float a2[2], gp2[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float g = accG[mt][r + k];
+          const float u = accU[mt][r + k];
+          const float s = sigmoid_fast(g);
+          const float a = g * s;
+          const float h = a * u;
+          a2[k] = a;
+          Hf[mt][r + k] = h;
+          gp2[k] = fmaf(-h, s, fmaf(u, s, h));
+        }
+        Ap[mt][r / 2] = pack_bf16x2(a2[0], a2[1]);
+        GPp[mt][r / 2] = pack_bf16x2(gp2[0], gp2[1]);
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) Hop[ks] = pack8(&Hf[ks >> 1][8 * (ks & 1)]);
-    {
-      const int hid = 32 * w + l32;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 hv = as_u32x4(Hop[ks]);
-        const int t0 = 32 * (ks >> 1) + 16 * (ks & 1) + 4 * hh;
-        st8(&sm.H[hid * HPT + t0], u32x2{hv[0], hv[1]});
-        st8(&sm.H[hid * HPT + t0 + 8], u32x2{hv[2], hv[3]});
-      }
+    for (int ks = 0; ks < 4; ++ks) {
+      Hop[ks] = pack8(&Hf[ks >> 1][8 * (ks & 1)]);
+      const u32x4 hv = as_u32x4(Hop[ks]);
+      lu16* hp = lds + OFF_H + o_hst + 32 * (ks >> 1) + 16 * (ks & 1);
+      lst8(hp, u32x2{hv[0], hv[1]});
+      lst8(hp + 8, u32x2{hv[2], hv[3]});
     }
     // Stage tile i+1 (loaded during the previous tile) and start loading i+2.
     if (i + 1 < nt) {
-      store_tile((i + 1) % KV_BUFS);
+      store_tile(i + 1);
       if (i + 2 < nt) load_tile(i + 2);
     }
     __syncthreads();  // B1: H(i) complete
@@ -266,17 +314,13 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
       f32x16 accY = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const int hr = 16 * ks + 8 * hh + jr;
-        const int tc = 32 * tb + cb + 4 * q4;
-        const bf16x8 a = tr_op(&sm.H[hr * HPT + tc], &sm.H[(hr + 4) * HPT + tc]);
-        accY = mfma32(a, WdB[ks], accY);
+        const lu16* hp = lds + OFF_H + o_htr + 16 * ks * HPT + 32 * tb;
+        const lu16* wp = lds + OFF_W + o_wtr + 16 * ks * WP + 32 * ob;
+        accY = mfma32(ltr_op(hp, hp + 4 * HPT), ltr_op(wp, wp + 4 * WP), accY);
       }
-      const int o = 32 * ob + l32;
-      uint16_t* Yc = sm.Y[yb];
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const int t0 = 32 * tb + 8 * rg + 4 * hh;
-        const u32x2 vn = lds_tr16(&Vc[(t0 + jr) * TP + 32 * ob + cb + 4 * q4]);
+        const u32x2 vn = ltr(Vc + o_tr + (32 * tb + 8 * rg) * TP + 32 * ob);
         const float r0 = accY[4 * rg + 0] + bf16_lo(vn[0]);
         const float r1 = accY[4 * rg + 1] + bf16_hi(vn[0]);
         const float r2 = accY[4 * rg + 2] + bf16_lo(vn[1]);
@@ -285,32 +329,33 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
         loss = fmaf(r1, r1, loss);
         loss = fmaf(r2, r2, loss);
         loss = fmaf(r3, r3, loss);
-        st8(&Yc[o * TP + t0], u32x2{pack_bf16x2(accY[4 * rg + 0], accY[4 * rg + 1]),
-                                    pack_bf16x2(accY[4 * rg + 2], accY[4 * rg + 3])});
+        lst8(Yc + o_yst + 8 * rg, u32x2{pack_bf16x2(accY[4 * rg + 0], accY[4 * rg + 1]),
+                                        pack_bf16x2(accY[4 * rg + 2], accY[4 * rg + 3])});
       }
     }
     __syncthreads();  // B2: Y(i) complete
 
     // dH = (Y - V') W_d^T for this wave's hidden units; dU = dH A, dG = dH gp.
     {
-      const uint16_t* Yc = sm.Y[yb];
+      bf16x8 WdT[4];  // B[k = o][j = hid], o = 16ks + 8hh + jj, hid = 32w + l32
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) WdT[ks] = lop(lds + OFF_W + o_wrow + 16 * ks);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         f32x16 accH = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const int orow = 16 * ks + 8 * hh + jr;
-          const int tc = 32 * mt + cb + 4 * q4;
-          const bf16x8 ya = tr_op(&Yc[orow * TP + tc], &Yc[(orow + 4) * TP + tc]);
-          const bf16x8 va = ld_op(&Vc[(32 * mt + l32) * TP + 16 * ks + 8 * hh]);
-          accH = mfma32(ya, WdTB[ks], accH);
-          accH = mfma32(va, WdTB[ks], accH);
+          const lu16* yp = Yc + o_ytr + 16 * ks * TP + 32 * mt;
+          accH = mfma32(ltr_op(yp, yp + 4 * TP), WdT[ks], accH);
+          accH = mfma32(lop(Vc + o_row + 32 * mt * TP + 16 * ks), WdT[ks], accH);
         }
         float dg[16], du[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          du[r] = accH[r] * Af[mt][r];
-          dg[r] = accH[r] * GP[mt][r];
+        for (int r = 0; r < 16; r += 2) {
+          du[r] = accH[r] * bf16_lo(Ap[mt][r / 2]);
+          du[r + 1] = accH[r + 1] * bf16_hi(Ap[mt][r / 2]);
+          dg[r] = accH[r] * bf16_lo(GPp[mt][r / 2]);
+          dg[r + 1] = accH[r + 1] * bf16_hi(GPp[mt][r / 2]);
         }
         dGop[2 * mt] = pack8(&dg[0]);
         dGop[2 * mt + 1] = pack8(&dg[8]);
@@ -339,10 +384,10 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
     }
   }
   loss = wave_sum(loss);
-  if (lane == 0) sm.red[w] = loss;
+  if (lane == 0) red[w] = loss;
   __syncthreads();
   if (tid == 0)
-    loss_part[(int64_t)head * P + chunk] = ((sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3])) * (1.0f / D);
+    loss_part[(int64_t)head * P + chunk] = ((red[0] + red[1]) + (red[2] + red[3])) * (1.0f / D);
 }
 
 }  // namespace
