@@ -92,6 +92,17 @@ __device__ __forceinline__ bf16x8 lpair_op(const lu16* p0, const lu16* p1) {
   return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
 }
 
+// Keeps a value in accumulation registers: MFMA reads its A/B operands from
+// them directly, which leaves the architectural VGPRs for in-flight LDS data.
+#ifndef VGGT3_PIN_AGPR
+#define VGGT3_PIN_AGPR 1
+#endif
+__device__ __forceinline__ void to_agpr(bf16x8& v) {
+#if VGGT3_PIN_AGPR
+  asm volatile("" : "+a"(v));
+#endif
+}
+
 __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
     const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg, const float* __restrict__ theta,
     float* __restrict__ part, float* __restrict__ loss_part, int64_t n_tokens, int n_heads, int P,
@@ -134,6 +145,8 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
       }
       WgB[ks] = pack8(g);
       WuB[ks] = pack8(u);
+      to_agpr(WgB[ks]);
+      to_agpr(WuB[ks]);
     }
   }
   // W_d (bf16) in LDS, natural [hid][o] layout.
@@ -361,6 +374,10 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
         dGop[2 * mt + 1] = pack8(&dg[8]);
         dUop[2 * mt] = pack8(&du[0]);
         dUop[2 * mt + 1] = pack8(&du[8]);
+        to_agpr(dGop[2 * mt]);
+        to_agpr(dGop[2 * mt + 1]);
+        to_agpr(dUop[2 * mt]);
+        to_agpr(dUop[2 * mt + 1]);
       }
     }
   }
