@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "TTT-layer tokens/sec (write+read) at 1000 views; % bf16 MFMA peak"
 GRAD_KERNEL = "grad_partial_bf16_kernel"
-GRAD_SOURCE = os.path.join(ROOT, "test_layer_amd", "csrc", "ttt_bf16.hip")
+GRAD_SOURCE = os.path.join(ROOT, "test_layer_amd", "csrc", "ttt_write_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grad_partial_bf16_views1000_traffic.json")
 
 
@@ -60,7 +60,7 @@ def load_traffic():
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(inp, cfg, target_s=15.0, max_views=64):
+def cpu_baseline(inp, cfg, target_s=15.0, max_views=256):
     """The fp64 CPU oracle, as it stands, on the first s views of the same
     scene (conv, `steps` write steps over those tokens, read). s doubles from
     2 views until one run takes >= target_s / 2 (or max_views)."""
