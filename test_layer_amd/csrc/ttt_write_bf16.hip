@@ -19,7 +19,7 @@
 //
 // MFMA layout (v_mfma_f32_32x32x16_bf16): a C tile keeps rows in registers and
 // columns across lanes, and is reused as an operand of any contraction over
-// its rows. Tokens are the rows of G, U, Y, dH, so H, dG and dU feed the
+// its rows. Tokens are the rows of G, U, dH, so H, dG and dU feed the
 // weight-gradient contractions (over tokens) straight from registers. The
 // remaining operand orders come from LDS, with ds_read_b64_tr_b16 transposing
 // 4x16 blocks on the way into registers.
@@ -28,13 +28,14 @@
 // dG, dU for those units and the matching gradient slices gW_g[:, w-slice],
 // gW_u[:, w-slice], gW_d[w-slice, :] (96 fp32 accumulators per lane, kept for
 // the whole chunk). W_g / W_u operands live in registers, W_d in LDS. Per
-// 64-token tile c the workgroup runs
-//   B0 | G,U(c) ; gradients(c-1) ; SwiGLU(c) -> H ; stage K,V'(c+1)
-//   B1 | Y(c) = H W_d ; R, loss ; Y -> LDS
-//   B2 | dH(c) = (Y - V') W_d^T ; dG, dU
-// so the gradient MFMAs of one tile overlap the SwiGLU VALU work of the next.
-// K and V' tiles rotate through 3 LDS buffers and Y through 2; global loads of
-// tile c+2 are issued while tile c computes. All LDS addressing is 32-bit.
+// 32-token tile c the workgroup runs
+//   B0 | G,U(c) ; SwiGLU(c) -> H ; stage K,V'(c+1), load c+2
+//   B1 | Y(c) = H W_d (16x16x32 MFMA tiles over all hidden units) ; loss ; Y -> LDS
+//   B2 | dH(c) = (Y - V') W_d^T ; dG, dU ; gW_d, gW_g, gW_u += tile c
+// The kernel is sized (about 50 KB of LDS, at most 256 registers per lane, all
+// of them architectural VGPRs, so MFMA results need no copies before VALU use)
+// so that two workgroups share a CU: while one waits at a barrier or on LDS,
+// the other's MFMA and VALU work fills the SIMDs. All LDS addressing is 32-bit.
 #include "bf16_ops.hpp"
 #include "kernels.hpp"
 
@@ -42,7 +43,7 @@
 #define VGGT3_WRITE_TP 72
 #endif
 #ifndef VGGT3_WRITE_HP
-#define VGGT3_WRITE_HP 72
+#define VGGT3_WRITE_HP 36
 #endif
 #ifndef VGGT3_WRITE_WP
 #define VGGT3_WRITE_WP 72
@@ -53,30 +54,29 @@ namespace {
 
 constexpr int D = 64;      // inputs / outputs of T per head
 constexpr int M = 128;     // hidden units
-constexpr int T = 64;      // tokens per tile
+constexpr int T = 32;      // tokens per tile
 constexpr int DM = D * M;
 constexpr int PER_HEAD = 3 * DM;
-constexpr int TP = VGGT3_WRITE_TP;   // pitch (elements) of [64][64] tiles: K[t][e], Vn[t][o], Y[o][t]
+constexpr int TP = VGGT3_WRITE_TP;   // pitch (elements) of [32][64] token tiles: K, -V', Y (all [t][ch])
 constexpr int HPT = VGGT3_WRITE_HP;  // pitch of H[hid][t]
 constexpr int WP = VGGT3_WRITE_WP;   // pitch of W_d[hid][o]
-constexpr int KV_BUFS = 3;
-constexpr int Y_BUFS = 2;
+constexpr int KV_BUFS = 2;
 constexpr int TSZ = T * TP;          // elements per token tile
 
 // LDS map (elements of bf16).
 constexpr int OFF_K = 0;
 constexpr int OFF_V = OFF_K + KV_BUFS * TSZ;
 constexpr int OFF_Y = OFF_V + KV_BUFS * TSZ;
-constexpr int OFF_H = OFF_Y + Y_BUFS * TSZ;
+constexpr int OFF_H = OFF_Y + TSZ;
 constexpr int OFF_W = OFF_H + M * HPT;
 constexpr int LDS_ELEMS = OFF_W + M * WP;
+static_assert(LDS_ELEMS * 2 <= 80 * 1024, "two workgroups per CU");
 
 typedef __attribute__((address_space(3))) uint16_t lu16;
 typedef __attribute__((address_space(3))) u32x4 lu32x4;
 typedef __attribute__((address_space(3))) u32x2 lu32x2;
 
 __device__ __forceinline__ u32x4 lld16(const lu16* p) { return *(const lu32x4*)p; }
-__device__ __forceinline__ u32x2 lld8(const lu16* p) { return *(const lu32x2*)p; }
 __device__ __forceinline__ void lst16(lu16* p, const u32x4& v) { *(lu32x4*)p = v; }
 __device__ __forceinline__ void lst8(lu16* p, const u32x2& v) { *(lu32x2*)p = v; }
 __device__ __forceinline__ u32x2 ltr(const lu16* p) {
@@ -87,23 +87,16 @@ __device__ __forceinline__ bf16x8 ltr_op(const lu16* p0, const lu16* p1) {
   const u32x2 a = ltr(p0), b = ltr(p1);
   return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
 }
-__device__ __forceinline__ bf16x8 lpair_op(const lu16* p0, const lu16* p1) {
-  const u32x2 a = lld8(p0), b = lld8(p1);
-  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+
+// 16x16x32 bf16 MFMA, fp32 accumulate.
+//   A operand: lane l holds A[row = l%16][k = 8*(l/16) + j], j = 0..7
+//   B operand: lane l holds B[k = 8*(l/16) + j][col = l%16]
+//   C/D:       lane l, register r holds C[row = 4*(l/16) + r][col = l%16]
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Keeps a value in accumulation registers: MFMA reads its A/B operands from
-// them directly, which leaves the architectural VGPRs for in-flight LDS data.
-#ifndef VGGT3_PIN_AGPR
-#define VGGT3_PIN_AGPR 1
-#endif
-__device__ __forceinline__ void to_agpr(bf16x8& v) {
-#if VGGT3_PIN_AGPR
-  asm volatile("" : "+a"(v));
-#endif
-}
-
-__global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
     const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg, const float* __restrict__ theta,
     float* __restrict__ part, float* __restrict__ loss_part, int64_t n_tokens, int n_heads, int P,
     int64_t n_blocks) {
@@ -119,11 +112,14 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
   const int w = tid >> 6;
   const int l32 = lane & 31;
   const int hh = lane >> 5;               // k-half of a 32x32x16 operand
-  const int cb = 16 * ((lane >> 4) & 1);  // column base of this lane's 16-lane group
+  const int g4 = lane >> 4;               // k-quarter of a 16x16x32 operand
+  const int i16 = lane & 15;
+  const int cb = 16 * ((lane >> 4) & 1);  // column base of this lane's 16-lane group (32-wide reads)
   const int jr = (lane & 15) >> 2;        // transpose-read source row within the group
   const int q4 = lane & 3;                // transpose-read source column quad
   const int64_t C = (int64_t)n_heads * D;
-  const int tb = w >> 1, ob = w & 1;      // this wave's Y tile (tokens 32tb.., outputs 32ob..)
+  const int tb = w >> 1;                  // this wave's Y rows: tokens 16tb..16tb+15
+  const int ob = 2 * (w & 1);             // and Y column blocks ob, ob+1 (16 outputs each)
 
   const float* th = theta + (int64_t)head * PER_HEAD;
   const float* Wg = th;
@@ -145,8 +141,6 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
       }
       WgB[ks] = pack8(g);
       WuB[ks] = pack8(u);
-      to_agpr(WgB[ks]);
-      to_agpr(WuB[ks]);
     }
   }
   // W_d (bf16) in LDS, natural [hid][o] layout.
@@ -170,87 +164,36 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
   const int nt = (int)(n_tiles_all * (chunk + 1) / P - tile_begin);
 
   // Lane-constant LDS offsets (elements).
-  const int o_row = l32 * TP + 8 * hh;                    // row-major operand rows (b128)
-  const int o_tr = (4 * hh + jr) * TP + cb + 4 * q4;       // transpose reads over token rows
-  const int o_htr = (8 * hh + jr) * HPT + cb + 4 * q4;     // transpose reads of H[hid][t]
-  const int o_ytr = (8 * hh + jr) * TP + cb + 4 * q4;      // transpose reads of Y[o][t]
-  const int o_wtr = (8 * hh + jr) * WP + cb + 4 * q4;      // transpose reads of W_d[hid][o]
-  const int o_wrow = (32 * w + l32) * WP + 8 * hh;         // W_d rows of this wave's units
-  const int o_yrow = l32 * TP + 4 * hh;                    // Y[o][t] runs for gW_d
-  const int o_hst = (32 * w + l32) * HPT + 4 * hh;         // H stores
-  const int o_yst = (32 * ob + l32) * TP + 32 * tb + 4 * hh;  // Y stores
+  const int o_row = l32 * TP + 8 * hh;                     // token-row operand reads (b128)
+  const int o_tr = (4 * hh + jr) * TP + cb + 4 * q4;        // transpose reads over token rows
+  const int o_hst = (32 * w + l32) * HPT + 4 * hh;          // H stores
+  const int o_ha = (8 * g4 + jr) * HPT + 16 * tb + 4 * q4;  // Y phase: H^T reads (A operand)
+  const int o_wb = (8 * g4 + jr) * WP + 16 * ob + 4 * q4;   // Y phase: W_d reads (B operand)
+  const int o_vl = (16 * tb + 4 * g4 + jr) * TP + 16 * ob + 4 * q4;  // Y phase: -V' at the C positions
+  const int o_yst = (16 * tb + 4 * g4) * TP + 16 * ob + i16;         // Y stores (4 rows)
+  const int o_wrow = (32 * w + l32) * WP + 8 * hh;          // W_d rows of this wave's units
 
-  // Tile staging: thread -> rows (tid>>3) and (tid>>3)+32, 8 channels at (tid&7)*8.
-  // Loads are unconditional (rows past the end re-read the last token and are
-  // zeroed), which keeps the compiler's load-counter waits exact.
+  // Tile staging: thread -> row tid>>3, 8 channels at (tid&7)*8. Loads are
+  // unconditional (rows past the end re-read the last token and are zeroed),
+  // which keeps the compiler's load-counter waits exact.
   const int srow = tid >> 3, scol = (tid & 7) * 8;
   const int o_stage = srow * TP + scol;
   const uint16_t* Kh = Kg + (int64_t)head * D + scol;
   const uint16_t* Vh = Vg + (int64_t)head * D + scol;
-  u32x4 kr[2], vr[2];
+  u32x4 kr, vr;
   auto load_tile = [&](int i) {
-    const int64_t tok0 = (tile_begin + i) * T;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      int64_t tok = tok0 + srow + 32 * s;
-      tok = tok < n_tokens ? tok : n_tokens - 1;
-      kr[s] = ld16(Kh + tok * C);
-      vr[s] = ld16(Vh + tok * C);
-    }
+    int64_t tok = (tile_begin + i) * T + srow;
+    tok = tok < n_tokens ? tok : n_tokens - 1;
+    kr = ld16(Kh + tok * C);
+    vr = ld16(Vh + tok * C);
   };
   auto store_tile = [&](int i) {
     const int buf = i % KV_BUFS;
-    const int64_t tok0 = (tile_begin + i) * T;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bool ok = tok0 + srow + 32 * s < n_tokens;
-      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-      lst16(lds + OFF_K + buf * TSZ + o_stage + 32 * s * TP, ok ? kr[s] : z);
-      lst16(lds + OFF_V + buf * TSZ + o_stage + 32 * s * TP,
-            ok ? (vr[s] ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}) : z);
-    }
-  };
-
-  // Operands of the previous tile's gradient contractions (k-slot jj of k-step
-  // ks is token 16ks + 8(jj/4) + 4hh + jj%4, the register order of C tiles).
-  // They start at zero, with zeroed "tile -1" buffers, so the gradient step
-  // runs unconditionally inside the loop body and adds nothing the first time.
-  bf16x8 Hop[4], dGop[4], dUop[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    Hop[ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-    dGop[ks] = Hop[ks];
-    dUop[ks] = Hop[ks];
-  }
-  for (int idx = tid * 8; idx < TSZ; idx += 256 * 8) {
-    lst16(lds + OFF_K + (KV_BUFS - 1) * TSZ + idx, u32x4{0u, 0u, 0u, 0u});
-    lst16(lds + OFF_V + (KV_BUFS - 1) * TSZ + idx, u32x4{0u, 0u, 0u, 0u});
-    lst16(lds + OFF_Y + (Y_BUFS - 1) * TSZ + idx, u32x4{0u, 0u, 0u, 0u});
-  }
-
-  auto gradients = [&](int kvb, int yb) {
-    const lu16* Kp = lds + OFF_K + kvb * TSZ;
-    const lu16* Vp = lds + OFF_V + kvb * TSZ;
-    const lu16* Yp = lds + OFF_Y + yb * TSZ;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const lu16* yr = Yp + o_yrow + 32 * nb * TP + 16 * ks;
-        const bf16x8 yB = lpair_op(yr, yr + 8);
-        const lu16* vt = Vp + o_tr + 16 * ks * TP + 32 * nb;
-        const bf16x8 vB = ltr_op(vt, vt + 8 * TP);
-        accWd[nb] = mfma32(Hop[ks], yB, accWd[nb]);
-        accWd[nb] = mfma32(Hop[ks], vB, accWd[nb]);
-      }
-#pragma unroll
-      for (int eb = 0; eb < 2; ++eb) {
-        const lu16* kt = Kp + o_tr + 16 * ks * TP + 32 * eb;
-        const bf16x8 kA = ltr_op(kt, kt + 8 * TP);
-        accWg[eb] = mfma32(kA, dGop[ks], accWg[eb]);
-        accWu[eb] = mfma32(kA, dUop[ks], accWu[eb]);
-      }
-    }
+    const bool ok = (tile_begin + i) * T + srow < n_tokens;
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    lst16(lds + OFF_K + buf * TSZ + o_stage, ok ? kr : z);
+    lst16(lds + OFF_V + buf * TSZ + o_stage,
+          ok ? (vr ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}) : z);
   };
 
   if (nt > 0) {
@@ -259,59 +202,49 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
     if (nt > 1) load_tile(1);
   }
 
+  lu16* const Yt = lds + OFF_Y;
   for (int i = 0; i < nt; ++i) {
-    const int kvb = i % KV_BUFS;
-    const int yb = i & 1;
-    const lu16* Kc = lds + OFF_K + kvb * TSZ;
-    const lu16* Vc = lds + OFF_V + kvb * TSZ;
-    lu16* Yc = lds + OFF_Y + yb * TSZ;
-    __syncthreads();  // B0: K, V'(i) staged; everything of tile i-2 consumed
+    const lu16* Kc = lds + OFF_K + (i % KV_BUFS) * TSZ;
+    const lu16* Vc = lds + OFF_V + (i % KV_BUFS) * TSZ;
+    __syncthreads();  // B0: tile i staged; everything of tile i-1 consumed
 
-    // G, U of tile i: element (mt, r) is token 32mt + 8(r/4) + 4hh + r%4, unit 32w + l32.
-    f32x16 accG[2], accU[2];
+    // G, U (tokens x this wave's hidden units): element r is token
+    // 8(r/4) + 4hh + r%4, hidden unit 32w + l32.
+    f32x16 accG = f32x16{}, accU = f32x16{};
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      accG[mt] = f32x16{};
-      accU[mt] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = lop(Kc + o_row + 32 * mt * TP + 16 * ks);
-        accG[mt] = mfma32(a, WgB[ks], accG[mt]);
-        accU[mt] = mfma32(a, WuB[ks], accU[mt]);
-      }
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 a = lop(Kc + o_row + 16 * ks);
+      accG = mfma32(a, WgB[ks], accG);
+      accU = mfma32(a, WuB[ks], accU);
     }
-
-    gradients((i + KV_BUFS - 1) % KV_BUFS, (i + 1) & 1);  // tile i-1
 
     // SwiGLU: s = sigmoid(G), A = G s, H = A U, gp = U silu'(G) = U s + H (1 - s).
     // A and gp are kept as bf16 pairs until the backward step.
-    uint32_t Ap[2][8], GPp[2][8];
-    float Hf[2][16];
+    uint32_t Ap[8], GPp[8];
+    float Hf[16];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int r = 0; r < 16; r += 2) {
+      float a2[2], gp2[2];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float a2[2], gp2[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const float g = accG[mt][r + k];
-          const float u = accU[mt][r + k];
-          const float s = sigmoid_fast(g);
-          const float a = g * s;
-          const float h = a * u;
-          a2[k] = a;
-          Hf[mt][r + k] = h;
-          gp2[k] = fmaf(-h, s, fmaf(u, s, h));
-        }
-        Ap[mt][r / 2] = pack_bf16x2(a2[0], a2[1]);
-        GPp[mt][r / 2] = pack_bf16x2(gp2[0], gp2[1]);
+      for (int k = 0; k < 2; ++k) {
+        const float g = accG[r + k];
+        const float u = accU[r + k];
+        const float s = sigmoid_fast(g);
+        const float a = g * s;
+        const float h = a * u;
+        a2[k] = a;
+        Hf[r + k] = h;
+        gp2[k] = fmaf(-h, s, fmaf(u, s, h));
       }
+      Ap[r / 2] = pack_bf16x2(a2[0], a2[1]);
+      GPp[r / 2] = pack_bf16x2(gp2[0], gp2[1]);
     }
+    bf16x8 Hop[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      Hop[ks] = pack8(&Hf[ks >> 1][8 * (ks & 1)]);
+    for (int ks = 0; ks < 2; ++ks) {
+      Hop[ks] = pack8(&Hf[8 * ks]);
       const u32x4 hv = as_u32x4(Hop[ks]);
-      lu16* hp = lds + OFF_H + o_hst + 32 * (ks >> 1) + 16 * (ks & 1);
+      lu16* hp = lds + OFF_H + o_hst + 16 * ks;
       lst8(hp, u32x2{hv[0], hv[1]});
       lst8(hp + 8, u32x2{hv[2], hv[3]});
     }
@@ -322,66 +255,86 @@ __global__ __launch_bounds__(256, 1) void grad_partial_bf16_kernel(
     }
     __syncthreads();  // B1: H(i) complete
 
-    // Y tile (tokens 32tb.., outputs 32ob..) = H W_d; R = Y - V'; Y -> LDS [o][t].
+    // Y (tokens 16tb.., outputs 16(ob+b)..) = H W_d over all hidden units;
+    // R = Y - V'; Y -> LDS [t][o].
     {
-      f32x16 accY = f32x16{};
+      f32x4 accY[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const lu16* hp = lds + OFF_H + o_htr + 16 * ks * HPT + 32 * tb;
-        const lu16* wp = lds + OFF_W + o_wtr + 16 * ks * WP + 32 * ob;
-        accY = mfma32(ltr_op(hp, hp + 4 * HPT), ltr_op(wp, wp + 4 * WP), accY);
+      for (int ks = 0; ks < 4; ++ks) {
+        const lu16* hp = lds + OFF_H + o_ha + 32 * ks * HPT;
+        const bf16x8 ha = ltr_op(hp, hp + 4 * HPT);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const lu16* wp = lds + OFF_W + o_wb + 32 * ks * WP + 16 * b;
+          accY[b] = mfma16(ha, ltr_op(wp, wp + 4 * WP), accY[b]);
+        }
       }
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const u32x2 vn = ltr(Vc + o_tr + (32 * tb + 8 * rg) * TP + 32 * ob);
-        const float r0 = accY[4 * rg + 0] + bf16_lo(vn[0]);
-        const float r1 = accY[4 * rg + 1] + bf16_hi(vn[0]);
-        const float r2 = accY[4 * rg + 2] + bf16_lo(vn[1]);
-        const float r3 = accY[4 * rg + 3] + bf16_hi(vn[1]);
+      for (int b = 0; b < 2; ++b) {
+        const u32x2 vn = ltr(Vc + o_vl + 16 * b);
+        const float r0 = accY[b][0] + bf16_lo(vn[0]);
+        const float r1 = accY[b][1] + bf16_hi(vn[0]);
+        const float r2 = accY[b][2] + bf16_lo(vn[1]);
+        const float r3 = accY[b][3] + bf16_hi(vn[1]);
         loss = fmaf(r0, r0, loss);
         loss = fmaf(r1, r1, loss);
         loss = fmaf(r2, r2, loss);
         loss = fmaf(r3, r3, loss);
-        lst8(Yc + o_yst + 8 * rg, u32x2{pack_bf16x2(accY[4 * rg + 0], accY[4 * rg + 1]),
-                                        pack_bf16x2(accY[4 * rg + 2], accY[4 * rg + 3])});
+        const uint32_t y01 = pack_bf16x2(accY[b][0], accY[b][1]);
+        const uint32_t y23 = pack_bf16x2(accY[b][2], accY[b][3]);
+        lu16* yp = Yt + o_yst + 16 * b;
+        yp[0] = (uint16_t)y01;
+        yp[TP] = (uint16_t)(y01 >> 16);
+        yp[2 * TP] = (uint16_t)y23;
+        yp[3 * TP] = (uint16_t)(y23 >> 16);
       }
     }
     __syncthreads();  // B2: Y(i) complete
 
     // dH = (Y - V') W_d^T for this wave's hidden units; dU = dH A, dG = dH gp.
+    bf16x8 dGop[2], dUop[2];
     {
-      bf16x8 WdT[4];  // B[k = o][j = hid], o = 16ks + 8hh + jj, hid = 32w + l32
+      f32x16 accH = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) WdT[ks] = lop(lds + OFF_W + o_wrow + 16 * ks);
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 wdt = lop(lds + OFF_W + o_wrow + 16 * ks);  // B[k = o][j = hid]
+        accH = mfma32(lop(Yt + o_row + 16 * ks), wdt, accH);
+        accH = mfma32(lop(Vc + o_row + 16 * ks), wdt, accH);
+      }
+      float dg[16], du[16];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        f32x16 accH = f32x16{};
+      for (int r = 0; r < 16; r += 2) {
+        du[r] = accH[r] * bf16_lo(Ap[r / 2]);
+        du[r + 1] = accH[r + 1] * bf16_hi(Ap[r / 2]);
+        dg[r] = accH[r] * bf16_lo(GPp[r / 2]);
+        dg[r + 1] = accH[r + 1] * bf16_hi(GPp[r / 2]);
+      }
+      dGop[0] = pack8(&dg[0]);
+      dGop[1] = pack8(&dg[8]);
+      dUop[0] = pack8(&du[0]);
+      dUop[1] = pack8(&du[8]);
+    }
+
+    // Weight gradients of tile i (k-slot jj of k-step ks is token
+    // 16ks + 8(jj/4) + 4hh + jj%4, the register order of C tiles).
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const lu16* yp = Yc + o_ytr + 16 * ks * TP + 32 * mt;
-          accH = mfma32(ltr_op(yp, yp + 4 * TP), WdT[ks], accH);
-          accH = mfma32(lop(Vc + o_row + 32 * mt * TP + 16 * ks), WdT[ks], accH);
-        }
-        float dg[16], du[16];
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          du[r] = accH[r] * bf16_lo(Ap[mt][r / 2]);
-          du[r + 1] = accH[r + 1] * bf16_hi(Ap[mt][r / 2]);
-          dg[r] = accH[r] * bf16_lo(GPp[mt][r / 2]);
-          dg[r + 1] = accH[r + 1] * bf16_hi(GPp[mt][r / 2]);
-        }
-        dGop[2 * mt] = pack8(&dg[0]);
-        dGop[2 * mt + 1] = pack8(&dg[8]);
-        dUop[2 * mt] = pack8(&du[0]);
-        dUop[2 * mt + 1] = pack8(&du[8]);
-        to_agpr(dGop[2 * mt]);
-        to_agpr(dGop[2 * mt + 1]);
-        to_agpr(dUop[2 * mt]);
-        to_agpr(dUop[2 * mt + 1]);
+      for (int nb = 0; nb < 2; ++nb) {
+        const lu16* yt = Yt + o_tr + 16 * ks * TP + 32 * nb;
+        const lu16* vt = Vc + o_tr + 16 * ks * TP + 32 * nb;
+        accWd[nb] = mfma32(Hop[ks], ltr_op(yt, yt + 8 * TP), accWd[nb]);
+        accWd[nb] = mfma32(Hop[ks], ltr_op(vt, vt + 8 * TP), accWd[nb]);
+      }
+#pragma unroll
+      for (int eb = 0; eb < 2; ++eb) {
+        const lu16* kt = Kc + o_tr + 16 * ks * TP + 32 * eb;
+        const bf16x8 kA = ltr_op(kt, kt + 8 * TP);
+        accWg[eb] = mfma32(kA, dGop[ks], accWg[eb]);
+        accWu[eb] = mfma32(kA, dUop[ks], accWu[eb]);
       }
     }
   }
-  if (nt > 0) gradients((nt - 1) % KV_BUFS, (nt - 1) & 1);
 
   // Partials in theta layout, times 2/d.
   constexpr float kScale = 2.0f / D;
