@@ -6,22 +6,30 @@
 // flattened again; per its Appendix A note, camera and register tokens bypass
 // the conv. The conv is depthwise (one 3x3 filter per channel), zero padded.
 //
-// Design (HBM-bound stencil). One thread owns one (view, column x, segment of
-// SEG rows, 4-channel group). It issues the loads of all SEG+2 input rows of
-// its segment at columns x-1, x, x+1 at once (8 bytes each; about 18 KB in
-// flight per wave, which is what keeps HBM busy), then computes the SEG output
-// rows with a rotating 3x3 window of fp32 vectors in registers. The code is
-// straight-line: rows outside the grid load as zero and only the stores of
-// rows past the segment are skipped. Lanes of a wave cover consecutive channel
-// groups of one token (512 contiguous bytes per wave access); the x-1 / x+1
-// re-reads of neighbouring columns hit L1/L2, and workgroups are remapped so
-// that each XCD walks a contiguous range of columns.
+// Design (HBM-bound stencil). A work item is one (view, column x, segment of
+// SEG rows, block of up to 256 4-channel groups); a few workgroups per CU walk
+// the items with a grid stride (loading the filters once), and thread t owns
+// channel group 256*block + t. Everything that decides which taps exist (x at
+// a grid edge, the segment touching the top or bottom row) is therefore
+// uniform across the workgroup: the left/right edges select a template
+// instance, and rows outside the grid become scalar branches that skip those
+// taps instead of selecting zeros per element. Each thread issues the loads of
+// all SEG+2 input rows of its segment at columns x-1, x, x+1 at once (8 bytes
+// each; about 23 KB in flight per wave, which is what keeps HBM busy) from a
+// uniform row address plus its 32-bit lane offset, then computes the SEG
+// output rows with a rotating 3x3 window of fp32 vectors in registers. Lanes of
+// a wave cover consecutive channel groups of one token (512 contiguous bytes
+// per wave access); the x-1 / x+1 re-reads of neighbouring columns hit L1/L2,
+// and workgroups are remapped so that each XCD walks a contiguous range of
+// columns.
 //
 // Bit-exact contract: acc = +0; taps with the row offset outermost and the
 // column offset innermost; acc = fl(acc + fl(w*v)), never fused (this file is
 // compiled with -ffp-contract=off and the pragma below); out-of-grid taps see
-// v = 0, which leaves acc unchanged; the result is rounded to bf16 with ties
-// to even.
+// v = 0; the result is rounded to bf16 with ties to even. An out-of-grid tap
+// adds fl(w*0) = +-0 to an accumulator that is never -0 (it starts at +0 and a
+// round-to-nearest sum is -0 only if both terms are), which leaves it
+// unchanged, so such taps are skipped.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,7 +39,13 @@ namespace vggt3 {
 
 namespace {
 
-constexpr int SEG = 10;     // output rows per thread (37 rows -> 4 segments)
+#ifndef VGGT3_CONV_WG_PER_CU
+#define VGGT3_CONV_WG_PER_CU 8
+#endif
+#ifndef VGGT3_CONV_SEG
+#define VGGT3_CONV_SEG 13
+#endif
+constexpr int SEG = VGGT3_CONV_SEG;  // output rows per thread (37 rows -> 3 segments)
 constexpr int MAX_W = 4096;  // widest grid row accepted (no staging limit in this design)
 
 template <bool BF16>
@@ -63,116 +77,116 @@ struct ConvTraits<false> {
   }
 };
 
-// One output row: acc = sum over taps, row offset outermost, column innermost.
-__device__ __forceinline__ void conv_row(const float (&wt)[9][4], const float (&up)[3][4],
-                                         const float (&mid)[3][4], const float (&dn)[3][4], float (&acc)[4]) {
-#pragma unroll
-  for (int ch = 0; ch < 4; ++ch) acc[ch] = 0.0f;
-#pragma unroll
-  for (int b = 0; b < 3; ++b)
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) acc[ch] = acc[ch] + wt[b][ch] * up[b][ch];
-#pragma unroll
-  for (int b = 0; b < 3; ++b)
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) acc[ch] = acc[ch] + wt[3 + b][ch] * mid[b][ch];
-#pragma unroll
-  for (int b = 0; b < 3; ++b)
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) acc[ch] = acc[ch] + wt[6 + b][ch] * dn[b][ch];
-}
-
-template <bool BF16>
-__global__ __launch_bounds__(256) void shortconv_kernel(const char* __restrict__ V, char* __restrict__ Vp,
-                                                         const float* __restrict__ w, int64_t n_items,
-                                                         int grid_h, int grid_w, int n_special, int C,
-                                                         int n_seg, int64_t n_blocks) {
+// Output rows [y0, y0 + SEG) of one column for one channel group. HAS_L /
+// HAS_R: whether columns x-1 / x+1 exist. `in_col` points at (y = 0, x) of the
+// input patch grid, `out_col` likewise; `lane` is this thread's byte offset in
+// a token row; `row_bytes` is one token row, `grid_row` one patch-grid row.
+template <bool BF16, bool HAS_L, bool HAS_R>
+__device__ __forceinline__ void conv_segment(const char* in_col, char* out_col, uint32_t lane,
+                                             int64_t row_bytes, int64_t grid_row, int y0, int grid_h,
+                                             const float (&wt)[9][4]) {
   using Tr = ConvTraits<BF16>;
   typedef typename Tr::vec_t vec_t;
-  constexpr int VB = (int)sizeof(vec_t);  // bytes per 4-channel group
-  const int64_t blk = xcd_remap(blockIdx.x, n_blocks);
-  const int64_t item = blk * 256 + threadIdx.x;
-  if (item >= n_items) return;
-  // item -> (view, column x, segment, channel group); channel group fastest.
-  const int CG = C / 4;
-  const int cg = (int)(item % CG);
-  int64_t rest = item / CG;
-  const int seg = (int)(rest % n_seg);
-  rest /= n_seg;
-  const int x = (int)(rest % grid_w);
-  const int64_t view = rest / grid_w;
-  const int64_t row_bytes = (int64_t)C * Tr::ESZ;
-  const int64_t tpv = (int64_t)n_special + (int64_t)grid_h * grid_w;
-  const char* vview = V + view * tpv * row_bytes + (int64_t)cg * VB;
-  char* oview = Vp + view * tpv * row_bytes + (int64_t)cg * VB;
-
-  if (x == 0 && seg == 0) {
-    for (int s = 0; s < n_special; ++s)
-      *reinterpret_cast<vec_t*>(oview + s * row_bytes) = *reinterpret_cast<const vec_t*>(vview + s * row_bytes);
-  }
-
-  const int y0 = seg * SEG;
-  const int64_t grid_row = (int64_t)grid_w * row_bytes;  // bytes from one grid row to the next
-  const char* src = vview + (int64_t)n_special * row_bytes + (int64_t)x * row_bytes;  // (y = 0, x)
-  char* dst = oview + (int64_t)n_special * row_bytes + (int64_t)x * row_bytes;
-  const bool has_l = x > 0, has_r = x + 1 < grid_w;
-
-  // Loads of input rows y0-1 .. y0+SEG at columns x-1, x, x+1. Every load is
-  // issued (from a clamped, in-grid address) and taps outside the grid are
-  // then replaced by zero with a select: with no conditional loads the
-  // compiler's load-counter waits stay exact, so all 36 loads stay in flight.
-  const int xl = has_l ? -1 : 0, xr = has_r ? 1 : 0;
+  // All SEG+2 input rows, from in-grid (clamped) addresses; rows outside the
+  // grid are loaded but never used.
   vec_t raw[SEG + 2][3];
 #pragma unroll
   for (int k = 0; k < SEG + 2; ++k) {
     const int y = y0 - 1 + k;
     const int yc = y < 0 ? 0 : (y >= grid_h ? grid_h - 1 : y);
-    const char* p = src + (int64_t)yc * grid_row;
-    raw[k][0] = *reinterpret_cast<const vec_t*>(p + xl * row_bytes);
-    raw[k][1] = *reinterpret_cast<const vec_t*>(p);
-    raw[k][2] = *reinterpret_cast<const vec_t*>(p + xr * row_bytes);
+    const char* p = in_col + (int64_t)yc * grid_row;
+    if (HAS_L) raw[k][0] = *reinterpret_cast<const vec_t*>(p - row_bytes + lane);
+    raw[k][1] = *reinterpret_cast<const vec_t*>(p + lane);
+    if (HAS_R) raw[k][2] = *reinterpret_cast<const vec_t*>(p + row_bytes + lane);
   }
+  float win[3][3][4];  // widened rows, rotating: win[k % 3] holds input row y0 - 1 + k
+  auto widen_row = [&](int k) {
 #pragma unroll
-  for (int k = 0; k < SEG + 2; ++k) {
-    const int y = y0 - 1 + k;
-    const bool in = y >= 0 && y < grid_h;
-    if (!(in && has_l)) raw[k][0] = vec_t{};
-    if (!in) raw[k][1] = vec_t{};
-    if (!(in && has_r)) raw[k][2] = vec_t{};
-  }
-
-  float wt[9][4];
-#pragma unroll
-  for (int ch = 0; ch < 4; ++ch)
-#pragma unroll
-    for (int t = 0; t < 9; ++t) wt[t][ch] = w[(int64_t)(cg * 4 + ch) * 9 + t];
-
-  float rA[3][4], rB[3][4], rC[3][4], acc[4];
-  auto widen_row = [&](int k, float (&row)[3][4]) {
-#pragma unroll
-    for (int b = 0; b < 3; ++b) Tr::widen(raw[k][b], row[b]);
+    for (int b = 0; b < 3; ++b)
+      if ((b != 0 || HAS_L) && (b != 2 || HAS_R)) Tr::widen(raw[k][b], win[k % 3][b]);
   };
-  auto store_row = [&](int k) {
+  auto taps = [&](int a, int k, float (&acc)[4]) {  // row offset a (0..2) from window row k
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      if ((b == 0 && !HAS_L) || (b == 2 && !HAS_R)) continue;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) acc[ch] = acc[ch] + wt[3 * a + b][ch] * win[k % 3][b][ch];
+    }
+  };
+  widen_row(0);
+  widen_row(1);
+#pragma unroll
+  for (int k = 0; k < SEG; ++k) {
+    widen_row(k + 2);
     const int y = y0 + k;
-    if (y < grid_h) *reinterpret_cast<vec_t*>(dst + (int64_t)y * grid_row) = Tr::narrow(acc);
-  };
-  widen_row(0, rA);
-  widen_row(1, rB);
+    if (y >= grid_h) break;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (y > 0) taps(0, k, acc);
+    taps(1, k + 1, acc);
+    if (y + 1 < grid_h) taps(2, k + 2, acc);
+    // V' is not read again by this kernel: stream it past the caches, which
+    // keeps them for the input rows that neighbouring columns re-read.
+    __builtin_nontemporal_store(Tr::narrow(acc), reinterpret_cast<vec_t*>(out_col + (int64_t)y * grid_row + lane));
+  }
+}
+
+// Work item = (view, segment, column x, channel block), channel block fastest,
+// so consecutive workgroups read neighbouring columns of one segment.
+template <bool BF16>
+__global__ __launch_bounds__(256) void shortconv_kernel(const char* __restrict__ V, char* __restrict__ Vp,
+                                                         const float* __restrict__ w, int64_t n_work,
+                                                         int grid_h, int grid_w, int n_special, int C,
+                                                         int n_seg, int n_cblk) {
+  using Tr = ConvTraits<BF16>;
+  typedef typename Tr::vec_t vec_t;
+  constexpr int VB = (int)sizeof(vec_t);  // bytes per 4-channel group
+  const int CG = C / 4;
+  const int64_t row_bytes = (int64_t)C * Tr::ESZ;
+  const int64_t tpv = (int64_t)n_special + (int64_t)grid_h * grid_w;
+  const int64_t grid_row = (int64_t)grid_w * row_bytes;
+  const int64_t stride = gridDim.x;
+  float wt[9][4];
+  int wt_cblk = -1;
+  for (int64_t wi = xcd_remap(blockIdx.x, stride); wi < n_work; wi += stride) {
+    const int cblk = (int)(wi % n_cblk);
+    int64_t rest = wi / n_cblk;
+    const int x = (int)(rest % grid_w);
+    rest /= grid_w;
+    const int seg = (int)(rest % n_seg);
+    const int64_t view = rest / n_seg;
+    const int cg = cblk * 256 + (int)threadIdx.x;
+    if (cg >= CG) continue;
+    const uint32_t lane = (uint32_t)cg * VB;
+    const char* vview = V + view * tpv * row_bytes;
+    char* oview = Vp + view * tpv * row_bytes;
+
+    if (x == 0 && seg == 0) {
+      for (int s = 0; s < n_special; ++s)
+        *reinterpret_cast<vec_t*>(oview + s * row_bytes + lane) =
+            *reinterpret_cast<const vec_t*>(vview + s * row_bytes + lane);
+    }
+
+    if (cblk != wt_cblk) {  // the filters of this channel block, loaded once per block change
 #pragma unroll
-  for (int k = 0; k < SEG; k += 3) {
-    widen_row(k + 2, rC);
-    conv_row(wt, rA, rB, rC, acc);
-    store_row(k);
-    if (k + 1 < SEG) {
-      widen_row(k + 3, rA);
-      conv_row(wt, rB, rC, rA, acc);
-      store_row(k + 1);
+      for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+        for (int t = 0; t < 9; ++t) wt[t][ch] = w[(int64_t)(cg * 4 + ch) * 9 + t];
+      wt_cblk = cblk;
     }
-    if (k + 2 < SEG) {
-      widen_row(k + 4, rB);
-      conv_row(wt, rC, rA, rB, acc);
-      store_row(k + 2);
-    }
+
+    const int64_t col = ((int64_t)n_special + x) * row_bytes;
+    const char* in_col = vview + col;
+    char* out_col = oview + col;
+    const int y0 = seg * SEG;
+    const bool has_l = x > 0, has_r = x + 1 < grid_w;
+    if (has_l && has_r)
+      conv_segment<BF16, true, true>(in_col, out_col, lane, row_bytes, grid_row, y0, grid_h, wt);
+    else if (has_l)
+      conv_segment<BF16, true, false>(in_col, out_col, lane, row_bytes, grid_row, y0, grid_h, wt);
+    else if (has_r)
+      conv_segment<BF16, false, true>(in_col, out_col, lane, row_bytes, grid_row, y0, grid_h, wt);
+    else
+      conv_segment<BF16, false, false>(in_col, out_col, lane, row_bytes, grid_row, y0, grid_h, wt);
   }
 }
 
@@ -181,17 +195,19 @@ __global__ __launch_bounds__(256) void shortconv_kernel(const char* __restrict__
 hipError_t launch_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, int grid_h,
                             int grid_w, int n_special, int C, bool bf16, hipStream_t stream) {
   const int n_seg = (grid_h + SEG - 1) / SEG;
-  const int64_t n_items = n_views * grid_w * (int64_t)n_seg * (C / 4);
-  if (n_items == 0) return hipSuccess;
-  const int64_t n_blocks = (n_items + 255) / 256;
+  const int n_cblk = (C / 4 + 255) / 256;
+  const int64_t n_work = n_views * grid_w * (int64_t)n_seg * n_cblk;
+  if (n_work == 0) return hipSuccess;
+  // A few resident workgroups per CU walk the work items with a grid stride,
+  // so the filters are loaded once per workgroup rather than once per item.
+  const int64_t max_grid = (int64_t)VGGT3_CONV_WG_PER_CU * 256;
+  const unsigned n_blocks = (unsigned)(n_work < max_grid ? n_work : max_grid);
   if (bf16)
-    hipLaunchKernelGGL(shortconv_kernel<true>, dim3((unsigned)n_blocks), dim3(256), 0, stream,
-                       static_cast<const char*>(V), static_cast<char*>(Vp), w, n_items, grid_h, grid_w,
-                       n_special, C, n_seg, n_blocks);
+    hipLaunchKernelGGL(shortconv_kernel<true>, dim3(n_blocks), dim3(256), 0, stream, static_cast<const char*>(V),
+                       static_cast<char*>(Vp), w, n_work, grid_h, grid_w, n_special, C, n_seg, n_cblk);
   else
-    hipLaunchKernelGGL(shortconv_kernel<false>, dim3((unsigned)n_blocks), dim3(256), 0, stream,
-                       static_cast<const char*>(V), static_cast<char*>(Vp), w, n_items, grid_h, grid_w,
-                       n_special, C, n_seg, n_blocks);
+    hipLaunchKernelGGL(shortconv_kernel<false>, dim3(n_blocks), dim3(256), 0, stream, static_cast<const char*>(V),
+                       static_cast<char*>(Vp), w, n_work, grid_h, grid_w, n_special, C, n_seg, n_cblk);
   return hipGetLastError();
 }
 

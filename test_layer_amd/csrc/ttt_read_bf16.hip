@@ -119,17 +119,22 @@ __global__ __launch_bounds__(512, 2) void read_bf16_kernel(const uint16_t* __res
         }
       }
     }
-    if (valid) {
-      uint16_t* dst = O + t * C + (int64_t)head * D;
+    // Output row o of Y^T tile ot is 8q + 4hh + i (q = r/4, i = r%4) in lane
+    // half hh. Exchanging the q-odd quads of the low half with the q-even
+    // quads of the high half (v_permlane32_swap) gives every lane 8
+    // consecutive outputs, stored as one 16-byte write.
+    uint16_t* dst = O + t * C + (int64_t)head * D;
 #pragma unroll
-      for (int ot = 0; ot < 2; ++ot) {
+    for (int ot = 0; ot < 2; ++ot) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          u32x2 v;
-          v[0] = pack_bf16x2(accY[ot][4 * q4 + 0], accY[ot][4 * q4 + 1]);
-          v[1] = pack_bf16x2(accY[ot][4 * q4 + 2], accY[ot][4 * q4 + 3]);
-          *reinterpret_cast<u32x2*>(dst + 32 * ot + 8 * q4 + 4 * hh) = v;
-        }
+      for (int p = 0; p < 2; ++p) {
+        const f32x16& a = accY[ot];
+        const uint32_t y0 = pack_bf16x2(a[8 * p + 0], a[8 * p + 1]), y1 = pack_bf16x2(a[8 * p + 2], a[8 * p + 3]);
+        const uint32_t x0 = pack_bf16x2(a[8 * p + 4], a[8 * p + 5]), x1 = pack_bf16x2(a[8 * p + 6], a[8 * p + 7]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(y0, x0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(y1, x1, false, false);
+        if (valid)
+          *reinterpret_cast<u32x4*>(dst + 32 * ot + 16 * p + 8 * hh) = u32x4{s0[0], s1[0], s0[1], s1[1]};
       }
     }
   };
