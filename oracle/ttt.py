@@ -21,6 +21,15 @@ Readings taken where the pages are open (each is listed in the design notes):
   * ShortConv2D: depthwise 3x3 cross-correlation, stride 1, zero padding,
     no bias, one filter per channel, within one view; special tokens copied.
 
+The pages' own inner recipe is also here ([GRAPH] section 3.4, "The dot product
+loss" and "Muon optimizer for inner loop"; the Appendix A hyper-parameters):
+  * loss="dot": L_h = -sum_i T(k_i) . v'_i (the dot product to be maximised,
+    written as a loss to minimise), so dL/dY = -V';
+  * opt="muon": each per-head weight-matrix gradient is replaced by its
+    Newton-Schulz orthogonalisation (5 iterations of the quintic iteration of
+    Jordan et al., 2024, the method the pages name) before theta -= lr * update;
+    no momentum and no shape-dependent rescaling (the pages give neither).
+
 Everything here is float64 except ``shortconv``, whose result is defined bit for
 bit by a float32 evaluation order (the "conv contract").
 """
@@ -178,22 +187,27 @@ def swiglu_forward(X, Wg, Wu, Wd, act: str = "silu") -> dict:
     return {"G": G, "U": U, "S": S, "A": A, "H": H, "Y": Y}
 
 
-def head_grad(K, Vp, Wg, Wu, Wd, act: str = "silu", chunk: int = 32768):
+def head_grad(K, Vp, Wg, Wu, Wd, act: str = "silu", chunk: int = 32768, loss: str = "mse"):
     """Loss and gradient of one head's inner objective at (W_g, W_u, W_d).
 
-    L = sum_i (1/d) ||T(k_i) - v'_i||^2 (Eq. 3 of [GRAPH] with a squared-error
-    L_t). The gradient is accumulated over fixed token chunks, which Eq. 5 of
+    loss="mse": L = sum_i (1/d) ||T(k_i) - v'_i||^2 (Eq. 3 of [GRAPH] with a
+    squared-error L_t), dY = (2/d)(Y - V').
+    loss="dot": L = -sum_i T(k_i) . v'_i ([GRAPH] "The dot product loss", as a
+    quantity to minimise), dY = -V'.
+    The gradient is accumulated over fixed token chunks, which Eq. 5 of
     [GRAPH] ("Minibatch gradient decomposition") makes exact. Backward pass by
     the chain rule through T:
-        R = Y - V', dY = (2/d) R, g_Wd = H^T dY, dH = dY W_d^T,
+        g_Wd = H^T dY, dH = dY W_d^T,
         dU = dH * act(G), dG = dH * U * act'(G), g_Wg = K^T dG, g_Wu = K^T dU,
     with silu'(g) = s (1 + g (1 - s)), s = sigmoid(g).
     Returns (loss, g_Wg, g_Wu, g_Wd), all float64.
     """
+    if loss not in ("mse", "dot"):
+        raise ValueError(loss)
     K = np.asarray(K)
     Vp = np.asarray(Vp)
     n, d = K.shape
-    loss = 0.0
+    total = 0.0
     gWg = np.zeros_like(Wg)
     gWu = np.zeros_like(Wu)
     gWd = np.zeros_like(Wd)
@@ -201,9 +215,13 @@ def head_grad(K, Vp, Wg, Wu, Wd, act: str = "silu", chunk: int = 32768):
         k = np.asarray(K[s:s + chunk], dtype=np.float64)
         v = np.asarray(Vp[s:s + chunk], dtype=np.float64)
         f = swiglu_forward(k, Wg, Wu, Wd, act)
-        R = f["Y"] - v
-        loss += float(np.sum(R * R)) / d
-        dY = (2.0 / d) * R
+        if loss == "mse":
+            R = f["Y"] - v
+            total += float(np.sum(R * R)) / d
+            dY = (2.0 / d) * R
+        else:
+            total -= float(np.sum(f["Y"] * v))
+            dY = -v
         gWd += f["H"].T @ dY
         dH = dY @ Wd.T
         dU = dH * f["A"]
@@ -214,7 +232,7 @@ def head_grad(K, Vp, Wg, Wu, Wd, act: str = "silu", chunk: int = 32768):
             dG = np.zeros_like(dH)
         gWg += k.T @ dG
         gWu += k.T @ dU
-    return loss, gWg, gWu, gWd
+    return total, gWg, gWu, gWd
 
 
 def _head_cols(h: int, d: int) -> slice:
@@ -222,30 +240,38 @@ def _head_cols(h: int, d: int) -> slice:
 
 
 def ttt_grad(K, Vp, theta, n_heads: int, d: int, m: int, act: str = "silu",
-             chunk: int = 32768):
+             chunk: int = 32768, loss: str = "mse"):
     """Gradient of every head's inner loss at theta: (grad [H, 3dm], loss [H])."""
     theta = np.asarray(theta, dtype=np.float64).reshape(n_heads, 3 * d * m)
     grad = np.zeros_like(theta)
-    loss = np.zeros(n_heads)
+    per_head = np.zeros(n_heads)
     for h in range(n_heads):
         Wg, Wu, Wd = split_theta(theta[h], d, m)
         cols = _head_cols(h, d)
-        L, gg, gu, gd = head_grad(K[:, cols], Vp[:, cols], Wg, Wu, Wd, act, chunk)
+        L, gg, gu, gd = head_grad(K[:, cols], Vp[:, cols], Wg, Wu, Wd, act, chunk, loss)
         grad[h] = join_theta(gg, gu, gd)
-        loss[h] = L
-    return grad, loss
+        per_head[h] = L
+    return grad, per_head
 
 
-def ttt_loss(K, Vp, theta, n_heads: int, d: int, m: int, act: str = "silu") -> np.ndarray:
-    """Per-head inner loss sum_i (1/d)||T(k_i) - v'_i||^2 at theta (no gradient)."""
+def ttt_loss(K, Vp, theta, n_heads: int, d: int, m: int, act: str = "silu",
+             loss: str = "mse") -> np.ndarray:
+    """Per-head inner loss at theta (no gradient): sum_i (1/d)||T(k_i) - v'_i||^2
+    for loss="mse", -sum_i T(k_i) . v'_i for loss="dot"."""
     theta = np.asarray(theta, dtype=np.float64).reshape(n_heads, 3 * d * m)
     out = np.zeros(n_heads)
     for h in range(n_heads):
         Wg, Wu, Wd = split_theta(theta[h], d, m)
         cols = _head_cols(h, d)
         f = swiglu_forward(np.asarray(K[:, cols], dtype=np.float64), Wg, Wu, Wd, act)
-        R = f["Y"] - np.asarray(Vp[:, cols], dtype=np.float64)
-        out[h] = float(np.sum(R * R)) / d
+        v = np.asarray(Vp[:, cols], dtype=np.float64)
+        if loss == "mse":
+            R = f["Y"] - v
+            out[h] = float(np.sum(R * R)) / d
+        elif loss == "dot":
+            out[h] = -float(np.sum(f["Y"] * v))
+        else:
+            raise ValueError(loss)
     return out
 
 
@@ -254,15 +280,58 @@ def ttt_apply(theta, grad, lr: float) -> np.ndarray:
     return np.asarray(theta, dtype=np.float64) - lr * np.asarray(grad, dtype=np.float64)
 
 
+# Coefficients of the quintic Newton-Schulz iteration of the Muon optimiser
+# (Jordan et al., 2024, the method named by [GRAPH] "Muon optimizer for inner
+# loop"): X <- a X + (b A + c A^2) X with A = X X^T.
+NS_COEFFS = (3.4445, -4.7750, 2.0315)
+NS_EPS = 1e-7
+
+
+def newton_schulz(G, steps: int = 5) -> np.ndarray:
+    """Approximate orthogonalisation of a matrix by the Muon Newton-Schulz iteration.
+
+    X = G / (||G||_F + eps); a matrix with more rows than columns is handled
+    through its transpose (so X X^T is the smaller Gram matrix); then `steps`
+    times X <- a X + (b A + c A A) X with A = X X^T. In the singular basis of G
+    each step maps every singular value x to p(x) = a x + b x^3 + c x^5.
+    """
+    a, b, c = NS_COEFFS
+    X = np.asarray(G, dtype=np.float64)
+    tall = X.shape[0] > X.shape[1]
+    if tall:
+        X = X.T
+    X = X / (np.linalg.norm(X) + NS_EPS)
+    for _ in range(steps):
+        A = X @ X.T
+        B = b * A + c * (A @ A)
+        X = a * X + B @ X
+    return X.T if tall else X
+
+
+def muon_apply(theta, grad, lr: float, n_heads: int, d: int, m: int, ns_steps: int = 5) -> np.ndarray:
+    """theta - lr * NS(g) for each head's W_g, W_u and W_d gradient matrix."""
+    theta = np.asarray(theta, dtype=np.float64).reshape(n_heads, 3 * d * m)
+    grad = np.asarray(grad, dtype=np.float64).reshape(n_heads, 3 * d * m)
+    out = theta.copy()
+    for h in range(n_heads):
+        gg, gu, gd = split_theta(grad[h], d, m)
+        upd = join_theta(newton_schulz(gg, ns_steps), newton_schulz(gu, ns_steps),
+                         newton_schulz(gd, ns_steps))
+        out[h] = theta[h] - lr * upd
+    return out
+
+
 def ttt_write(K, Vp, theta0, n_heads: int, d: int, m: int, lr: float, steps: int,
-              act: str = "silu", reduction: str = "sum", chunk: int = 32768):
+              act: str = "silu", reduction: str = "sum", chunk: int = 32768,
+              loss: str = "mse", opt: str = "gd", ns_steps: int = 5):
     """Fit the fast weights: `steps` full-batch gradient-descent steps from theta0.
 
     Eq. 3 of [GRAPH] approximated by a fixed number of plain GD steps; each step
     is one pass over all n tokens at the current theta followed by one update
     with the accumulated gradient ([GRAPH] "Large-Scale Inference Strategies":
     accumulate over minibatches, then apply). ``reduction="mean"`` divides loss
-    and gradient by n (an alternative reading kept for tests only).
+    and gradient by n (an alternative reading kept for tests only). loss="dot"
+    and opt="muon" give the pages' own recipe (see the module notes).
     Returns (theta* [H, 3dm], losses [steps, H] at the theta each step starts
     from, grads [steps, H, 3dm]).
     """
@@ -271,14 +340,19 @@ def ttt_write(K, Vp, theta0, n_heads: int, d: int, m: int, lr: float, steps: int
     losses = np.zeros((steps, n_heads))
     grads = np.zeros((steps, n_heads, 3 * d * m))
     for s in range(steps):
-        g, L = ttt_grad(K, Vp, theta, n_heads, d, m, act, chunk)
+        g, L = ttt_grad(K, Vp, theta, n_heads, d, m, act, chunk, loss)
         if reduction == "mean":
             g, L = g / n, L / n
         elif reduction != "sum":
             raise ValueError(reduction)
         losses[s] = L
         grads[s] = g
-        theta = ttt_apply(theta, g, lr)
+        if opt == "gd":
+            theta = ttt_apply(theta, g, lr)
+        elif opt == "muon":
+            theta = muon_apply(theta, g, lr, n_heads, d, m, ns_steps)
+        else:
+            raise ValueError(opt)
     return theta, losses, grads
 
 
