@@ -35,11 +35,19 @@ GRAD_SOURCE = os.path.join(ROOT, "test_layer_amd", "csrc", "ttt_write_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grad_partial_bf16_views1000_traffic.json")
 
 
-def flops_per_token(cfg):
-    """Algorithmic flops per token: write step = 7 GEMM passes of 2*d*m per head
-    (G, U, Y forward; dH backward; three weight gradients); read = 3."""
+RECIPES = {
+    # name: (loss, optimizer, description)
+    "mse_gd": ("mse", "gd", "mean-squared inner loss, plain gradient descent"),
+    "dot_muon": ("dot", "muon", "the pages' recipe: dot-product inner loss, Muon update (5 Newton-Schulz steps)"),
+}
+
+
+def flops_per_token(cfg, loss="mse"):
+    """Algorithmic flops per token: a write step with the squared-error loss is
+    7 GEMM passes of 2*d*m per head (G, U, Y forward; dH backward; three weight
+    gradients); the dot-product loss needs no Y (dL/dY = -V'), so 6; read = 3."""
     per_gemm = 2 * cfg.d_head * cfg.d_hidden * cfg.n_heads
-    return 7 * per_gemm, 3 * per_gemm
+    return (7 if loss == "mse" else 6) * per_gemm, 3 * per_gemm
 
 
 def source_sha256(path):
@@ -47,11 +55,12 @@ def source_sha256(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic():
+def load_traffic(recipe="mse_gd"):
     """HBM bytes per launch of the gradient kernel from the committed rocprofv3
     counter summary, or None if absent or taken on different kernel source."""
+    path = TRAFFIC_FILE if recipe == "mse_gd" else TRAFFIC_FILE.replace("_views1000", f"_{recipe}_views1000")
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -60,7 +69,7 @@ def load_traffic():
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(inp, cfg, target_s=15.0, max_views=256):
+def cpu_baseline(inp, cfg, target_s=15.0, max_views=256, loss="mse", opt="gd"):
     """The fp64 CPU oracle, as it stands, on the first s views of the same
     scene (conv, `steps` write steps over those tokens, read). s doubles from
     2 views until one run takes >= target_s / 2 (or max_views)."""
@@ -87,7 +96,7 @@ def cpu_baseline(inp, cfg, target_s=15.0, max_views=256):
         t0 = time.perf_counter()
         Vp = oracle.shortconv(V, w, views, cfg.grid_h, cfg.grid_w, cfg.n_special, out="bf16")
         th, _, _ = oracle.ttt_write(K, Vp.astype(np.float64), th0, cfg.n_heads, cfg.d_head, cfg.d_hidden,
-                                    cfg.lr, cfg.steps)
+                                    cfg.lr, cfg.steps, loss=loss, opt=opt)
         oracle.ttt_read(Q, th, cfg.n_heads, cfg.d_head, cfg.d_hidden)
         dt = time.perf_counter() - t0
         if dt >= target_s / 2 or views >= max_views or views * 2 > cfg.n_views:
@@ -110,6 +119,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="views1000")
+    ap.add_argument("--recipe", default="mse_gd", choices=sorted(RECIPES),
+                    help="inner loss and update rule (default: squared error + gradient descent)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (counter calibration)")
@@ -127,6 +138,7 @@ def main():
     from synth import CONFIGS, make_inputs
 
     cfg = CONFIGS[args.config]
+    loss_kind, opt_kind, recipe_desc = RECIPES[args.recipe]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = make_inputs(cfg, dev)
@@ -137,6 +149,7 @@ def main():
     theta = inp.theta0.clone()
     ws = tla.make_workspace(n, H, d, m, dt_code, dev)
     loss = torch.zeros((cfg.steps, H), device=dev)
+    gbuf = torch.empty_like(theta)
     nq = inp.Q.shape[0]
 
     def step(ev=None):
@@ -149,10 +162,14 @@ def main():
         for s in range(cfg.steps):
             if ev:
                 ev["g"][s][0].record()
-            tla.ttt_grad_partials(inp.K, Vp, theta, H, ws)
+            tla.ttt_grad_partials(inp.K, Vp, theta, H, ws, loss=loss_kind)
             if ev:
                 ev["g"][s][1].record()
-            tla.ttt_reduce(ws, n, H, d, m, dt_code, tla.REDUCE_APPLY, theta, cfg.lr, loss[s])
+            if opt_kind == "gd":
+                tla.ttt_reduce(ws, n, H, d, m, dt_code, tla.REDUCE_APPLY, theta, cfg.lr, loss[s])
+            else:
+                tla.ttt_reduce(ws, n, H, d, m, dt_code, tla.REDUCE_STORE, gbuf, 0.0, loss[s])
+                tla.ttt_muon_apply(theta, gbuf, cfg.lr, H, d, m, 5)
         if ev:
             ev["w1"].record()
         tla.ttt_read(inp.Q, theta, H, out=O)
@@ -183,7 +200,7 @@ def main():
     grad_ms = [a.elapsed_time(b) for e in events for (a, b) in e["g"]]
     grad_avg_ms = sum(grad_ms) / len(grad_ms)
 
-    fw, fr = flops_per_token(cfg)
+    fw, fr = flops_per_token(cfg, loss_kind)
     grad_flops = fw * n  # per launch of the gradient kernel
     achieved = grad_flops / (grad_avg_ms * 1e-3) / 1e12
     mlp_frac = (fw * n * cfg.steps + fr * nq) / ((write_ms + read_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
@@ -214,7 +231,7 @@ def main():
             "workload": f"{cfg.name}: {cfg.description}",
             "n_views": cfg.n_views, "tokens_per_view": cfg.tokens_per_view, "n_tokens": n,
             "n_heads": H, "d_head": d, "d_hidden": m, "write_steps": cfg.steps, "lr": cfg.lr,
-            "read_tokens": nq, "parallelism": "single GPU",
+            "read_tokens": nq, "parallelism": "single GPU", "recipe": f"{args.recipe}: {recipe_desc}",
         },
         "roofline": {
             "bound": "mfma",
@@ -223,7 +240,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": load_traffic(),
+            "traffic": load_traffic(args.recipe),
             "avg_launch_ms": grad_avg_ms,
             "flops_per_launch": grad_flops,
         },
@@ -233,7 +250,7 @@ def main():
         "final_loss_head0": float(loss[-1, 0].item()),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, cfg)
+        res["cpu_baseline"] = cpu_baseline(inp, cfg, loss=loss_kind, opt=opt_kind)
     print(json.dumps(res), flush=True)
 
 

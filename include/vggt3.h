@@ -65,6 +65,24 @@ enum {
 
 enum { VGGT3_BF16 = 0, VGGT3_F32 = 1 };
 
+/* Inner loss of the write:
+ *   VGGT3_LOSS_MSE  L_h = sum_i (1/d)||T(k_i) - v'_i||^2   (dL/dY = (2/d)(Y - V'))
+ *   VGGT3_LOSS_DOT  L_h = -sum_i T(k_i) . v'_i             (dL/dY = -V')
+ * The dot form is the pages' own ([GRAPH] "The dot product loss": the dot
+ * product is maximised, here written as a loss to minimise). */
+enum { VGGT3_LOSS_MSE = 0, VGGT3_LOSS_DOT = 1 };
+
+/* Update rule of one write step:
+ *   VGGT3_OPT_GD    theta <- theta - lr * g
+ *   VGGT3_OPT_MUON  theta <- theta - lr * NS(g) per head and weight matrix,
+ *                   NS = ns_steps iterations of the quintic Newton-Schulz
+ *                   orthogonalisation of the Muon optimiser ([GRAPH] "Muon
+ *                   optimizer for inner loop": 5 iterations, lr 0.1; the
+ *                   iteration and its coefficients 3.4445, -4.7750, 2.0315 are
+ *                   those of the named method, Jordan et al. 2024). No momentum. */
+enum { VGGT3_OPT_GD = 0, VGGT3_OPT_MUON = 1 };
+#define VGGT3_MAX_NS_STEPS 64
+
 /* Library version (major*10000 + minor*100 + patch). */
 int vggt3_version(void);
 
@@ -98,9 +116,10 @@ int vggt3_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, in
                     void* stream);
 
 /*
- * Bytes of device workspace vggt3_ttt_write / vggt3_ttt_grad need for this
- * problem (per-chunk fp32 gradient and loss partials of the Eq. 5 split).
- * Returns 0 for an unsupported shape.
+ * Bytes of device workspace vggt3_ttt_write / vggt3_ttt_grad (and their _ex
+ * forms) need for this problem: per-chunk fp32 gradient and loss partials of
+ * the Eq. 5 split, plus one reduced gradient for Muon steps. Returns 0 for an
+ * unsupported shape.
  */
 size_t vggt3_ttt_workspace_bytes(int64_t n_tokens, int32_t n_heads, int32_t d_head,
                                  int32_t d_hidden, int32_t dtype);
@@ -129,6 +148,18 @@ int vggt3_ttt_write(const void* K, const void* Vp, float* theta, int64_t n_token
                     void* stream);
 
 /*
+ * vggt3_ttt_write with a choice of inner loss (VGGT3_LOSS_*) and update rule
+ * (VGGT3_OPT_*); vggt3_ttt_write is the MSE / GD case. ns_steps (0 ..
+ * VGGT3_MAX_NS_STEPS) is used only with VGGT3_OPT_MUON; loss_out receives the
+ * chosen loss. Muon is supported for (d_head, d_hidden) = (64, 128) and
+ * (16, 32). Other arguments, errors and n_tokens == 0 as in vggt3_ttt_write.
+ */
+int vggt3_ttt_write_ex(const void* K, const void* Vp, float* theta, int64_t n_tokens, int32_t n_heads,
+                       int32_t d_head, int32_t d_hidden, float lr, int32_t steps, int32_t loss,
+                       int32_t optimizer, int32_t ns_steps, int32_t dtype, void* workspace,
+                       size_t workspace_bytes, float* loss_out, void* stream);
+
+/*
  * Gradient of the inner loss at theta over n_tokens tokens ([GRAPH] Eq. 5: the
  * full gradient is the sum of per-minibatch gradients, so chunks of a scene
  * can be fed in any number of calls with accumulate = 1).
@@ -142,6 +173,12 @@ int vggt3_ttt_grad(const void* K, const void* Vp, const float* theta, float* gra
                    int32_t accumulate, int64_t n_tokens, int32_t n_heads, int32_t d_head,
                    int32_t d_hidden, int32_t dtype, void* workspace, size_t workspace_bytes,
                    float* loss_out, void* stream);
+
+/* vggt3_ttt_grad for either inner loss (VGGT3_LOSS_*). */
+int vggt3_ttt_grad_ex(const void* K, const void* Vp, const float* theta, float* grad,
+                      int32_t accumulate, int64_t n_tokens, int32_t n_heads, int32_t d_head,
+                      int32_t d_hidden, int32_t loss, int32_t dtype, void* workspace,
+                      size_t workspace_bytes, float* loss_out, void* stream);
 
 /*
  * The two halves of vggt3_ttt_grad / one step of vggt3_ttt_write, for callers
@@ -170,9 +207,30 @@ int vggt3_ttt_grad_partials(const void* K, const void* Vp, const float* theta, i
                             int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* vggt3_ttt_grad_partials for either inner loss (VGGT3_LOSS_*); the reduce is
+ * the same for both. */
+int vggt3_ttt_grad_partials_ex(const void* K, const void* Vp, const float* theta, int64_t n_tokens,
+                               int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t loss,
+                               int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 int vggt3_ttt_reduce(const void* workspace, size_t workspace_bytes, int64_t n_tokens, int32_t n_heads,
                      int32_t d_head, int32_t d_hidden, int32_t dtype, int32_t mode, float* dst,
                      float lr, float* loss_out, void* stream);
+
+/*
+ * Muon update ([GRAPH] "Muon optimizer for inner loop"): for every head and
+ * each of its three weight matrices W_g [d][m], W_u [d][m], W_d [m][d]:
+ *   theta_W <- theta_W - lr * NS(grad_W),
+ * NS(G): X = G / (||G||_F + 1e-7), oriented with rows <= columns (W_d is
+ * transposed and back), then ns_steps times A = X X^T, X = a X + (b A + c A A) X
+ * with (a, b, c) = (3.4445, -4.7750, 2.0315); all in fp32, deterministic.
+ *   theta, grad  float32 [n_heads][3*d_head*d_hidden] (layout of theta); grad
+ *                read only and must not overlap theta.
+ *   ns_steps     0 .. VGGT3_MAX_NS_STEPS (0 applies the normalised gradient).
+ * Supported (d_head, d_hidden): (64, 128) and (16, 32).
+ */
+int vggt3_ttt_muon_apply(float* theta, const float* grad, float lr, int32_t n_heads, int32_t d_head,
+                         int32_t d_hidden, int32_t ns_steps, void* stream);
 
 /*
  * One plain gradient-descent update theta <- theta - lr * grad over

@@ -105,24 +105,48 @@ def _mlp_dims(theta: torch.Tensor, X: torch.Tensor, n_heads: int, d_hidden: Opti
     return d, m
 
 
+LOSS_MSE, LOSS_DOT = 0, 1
+OPT_GD, OPT_MUON = 0, 1
+_LOSSES = {"mse": LOSS_MSE, "dot": LOSS_DOT}
+_OPTS = {"gd": OPT_GD, "muon": OPT_MUON}
+
+
+def _loss_code(loss) -> int:
+    return _LOSSES[loss] if isinstance(loss, str) else int(loss)
+
+
+def _opt_code(opt) -> int:
+    return _OPTS[opt] if isinstance(opt, str) else int(opt)
+
+
 def ttt_write(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, lr: float, steps: int, n_heads: int,
               d_hidden: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-              loss_out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """`steps` gradient-descent steps of the inner loss; theta (fp32) is updated in place."""
+              loss_out: Optional[torch.Tensor] = None, loss="mse", optimizer="gd", ns_steps: int = 5) -> torch.Tensor:
+    """`steps` write steps of the inner loss; theta (fp32) is updated in place.
+
+    loss: "mse" (default) or "dot"; optimizer: "gd" (default) or "muon" with
+    `ns_steps` Newton-Schulz iterations.
+    """
     _check_dev(K, Vp, theta, workspace, loss_out)
     d, m = _mlp_dims(theta, K, n_heads, d_hidden)
     dt = _dtype_code(K)
     if workspace is None:
         workspace = make_workspace(K.shape[0], n_heads, d, m, dt, K.device)
     nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _call("vggt3_ttt_write", _ptr(K), _ptr(Vp), _ptr(theta), K.shape[0], n_heads, d, m, float(lr), int(steps),
-          dt, _ptr(workspace), nb, _ptr(loss_out), _stream())
+    lc, oc = _loss_code(loss), _opt_code(optimizer)
+    if lc == LOSS_MSE and oc == OPT_GD:
+        _call("vggt3_ttt_write", _ptr(K), _ptr(Vp), _ptr(theta), K.shape[0], n_heads, d, m, float(lr), int(steps),
+              dt, _ptr(workspace), nb, _ptr(loss_out), _stream())
+    else:
+        _call("vggt3_ttt_write_ex", _ptr(K), _ptr(Vp), _ptr(theta), K.shape[0], n_heads, d, m, float(lr),
+              int(steps), lc, oc, int(ns_steps), dt, _ptr(workspace), nb, _ptr(loss_out), _stream())
     return theta
 
 
 def ttt_grad(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, n_heads: int,
              grad: Optional[torch.Tensor] = None, accumulate: bool = False, d_hidden: Optional[int] = None,
-             workspace: Optional[torch.Tensor] = None, loss_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+             workspace: Optional[torch.Tensor] = None, loss_out: Optional[torch.Tensor] = None,
+             loss="mse") -> torch.Tensor:
     """Gradient of the inner loss at theta (Eq. 5 split: accumulate=True adds to grad)."""
     if grad is None:
         grad = torch.empty_like(theta)
@@ -132,8 +156,13 @@ def ttt_grad(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, n_heads: in
     if workspace is None:
         workspace = make_workspace(K.shape[0], n_heads, d, m, dt, K.device)
     nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _call("vggt3_ttt_grad", _ptr(K), _ptr(Vp), _ptr(theta), _ptr(grad), int(bool(accumulate)), K.shape[0],
-          n_heads, d, m, dt, _ptr(workspace), nb, _ptr(loss_out), _stream())
+    lc = _loss_code(loss)
+    if lc == LOSS_MSE:
+        _call("vggt3_ttt_grad", _ptr(K), _ptr(Vp), _ptr(theta), _ptr(grad), int(bool(accumulate)), K.shape[0],
+              n_heads, d, m, dt, _ptr(workspace), nb, _ptr(loss_out), _stream())
+    else:
+        _call("vggt3_ttt_grad_ex", _ptr(K), _ptr(Vp), _ptr(theta), _ptr(grad), int(bool(accumulate)), K.shape[0],
+              n_heads, d, m, lc, dt, _ptr(workspace), nb, _ptr(loss_out), _stream())
     return grad
 
 
@@ -141,12 +170,26 @@ REDUCE_APPLY, REDUCE_STORE, REDUCE_ACCUMULATE = 0, 1, 2
 
 
 def ttt_grad_partials(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, n_heads: int,
-                      workspace: torch.Tensor, d_hidden: Optional[int] = None) -> None:
+                      workspace: torch.Tensor, d_hidden: Optional[int] = None, loss="mse") -> None:
     """Per-(head, chunk) gradient and loss partials into `workspace` (Eq. 5 inner sums)."""
     _check_dev(K, Vp, theta, workspace)
     d, m = _mlp_dims(theta, K, n_heads, d_hidden)
-    _call("vggt3_ttt_grad_partials", _ptr(K), _ptr(Vp), _ptr(theta), K.shape[0], n_heads, d, m, _dtype_code(K),
-          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+    lc = _loss_code(loss)
+    if lc == LOSS_MSE:
+        _call("vggt3_ttt_grad_partials", _ptr(K), _ptr(Vp), _ptr(theta), K.shape[0], n_heads, d, m,
+              _dtype_code(K), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+    else:
+        _call("vggt3_ttt_grad_partials_ex", _ptr(K), _ptr(Vp), _ptr(theta), K.shape[0], n_heads, d, m, lc,
+              _dtype_code(K), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+
+
+def ttt_muon_apply(theta: torch.Tensor, grad: torch.Tensor, lr: float, n_heads: int, d_head: int,
+                   d_hidden: int, ns_steps: int = 5) -> torch.Tensor:
+    """theta -= lr * NS(grad) per head and weight matrix (Muon update), in place."""
+    _check_dev(theta, grad)
+    _call("vggt3_ttt_muon_apply", _ptr(theta), _ptr(grad), float(lr), n_heads, d_head, d_hidden, int(ns_steps),
+          _stream())
+    return theta
 
 
 def ttt_reduce(workspace: torch.Tensor, n_tokens: int, n_heads: int, d_head: int, d_hidden: int, dtype_code: int,
@@ -177,8 +220,9 @@ def ttt_read(Q: torch.Tensor, theta: torch.Tensor, n_heads: int, d_hidden: Optio
 
 
 def ttt_layer(K, V, Q, theta, conv_w, n_views, grid_h, grid_w, n_special, n_heads, lr, steps,
-              workspace=None, loss_out=None, Vp=None, O=None):
+              workspace=None, loss_out=None, Vp=None, O=None, loss="mse", optimizer="gd", ns_steps=5):
     """The whole layer: V' = ShortConv2D(V); write theta (in place); O = read(Q)."""
     Vp = shortconv(V, conv_w, n_views, grid_h, grid_w, n_special, out=Vp)
-    ttt_write(K, Vp, theta, lr, steps, n_heads, workspace=workspace, loss_out=loss_out)
+    ttt_write(K, Vp, theta, lr, steps, n_heads, workspace=workspace, loss_out=loss_out, loss=loss,
+              optimizer=optimizer, ns_steps=ns_steps)
     return ttt_read(Q, theta, n_heads, out=O), Vp

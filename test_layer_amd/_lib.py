@@ -35,6 +35,13 @@ SIGNATURES = {
                                  c_void_p, c_void_p]),
     "vggt3_ttt_apply": (c_int, [c_void_p, c_void_p, c_float, c_int, c_int, c_int, c_void_p]),
     "vggt3_ttt_read": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_int, c_int, c_int, c_int, c_void_p]),
+    "vggt3_ttt_write_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_int, c_int, c_int, c_float, c_int,
+                                   c_int, c_int, c_int, c_int, c_void_p, c_size, c_void_p, c_void_p]),
+    "vggt3_ttt_grad_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_i64, c_int, c_int, c_int,
+                                  c_int, c_int, c_void_p, c_size, c_void_p, c_void_p]),
+    "vggt3_ttt_grad_partials_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_int, c_int, c_int, c_int, c_int,
+                                           c_void_p, c_size, c_void_p]),
+    "vggt3_ttt_muon_apply": (c_int, [c_void_p, c_void_p, c_float, c_int, c_int, c_int, c_int, c_void_p]),
 }
 
 _lib = None

@@ -21,7 +21,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvggt3.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "shortconv.hip", "ttt_write_bf16.hip", "ttt_read_bf16.hip", "ttt_f32.hip", "reduce.hip"]
+SOURCES = ["api.hip", "shortconv.hip", "ttt_write_bf16.hip", "ttt_read_bf16.hip", "ttt_f32.hip", "reduce.hip",
+           "muon.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

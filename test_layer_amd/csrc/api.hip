@@ -74,28 +74,49 @@ int check_mlp(const MlpArgs& a) {
 size_t theta_bytes(const MlpArgs& a) { return (size_t)a.H * 3 * a.d * a.m * sizeof(float); }
 size_t token_bytes(const MlpArgs& a) { return (size_t)a.n * a.H * a.d * elem_size(a.dt); }
 
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Workspace: [per-chunk gradient partials | per-chunk loss partials | one
+// reduced gradient (the Muon step's input)], each 256-byte aligned.
+struct WsLayout {
+  size_t part, loss, grad, total;
+};
+WsLayout ws_layout(const MlpArgs& a, int P) {
+  WsLayout l;
+  l.part = 0;
+  l.loss = round256((size_t)a.H * P * 3 * a.d * a.m * sizeof(float));
+  l.grad = l.loss + round256((size_t)a.H * P * sizeof(float));
+  l.total = l.grad + round256((size_t)a.H * 3 * a.d * a.m * sizeof(float));
+  return l;
+}
+
 size_t workspace_bytes(const MlpArgs& a, int* P_out) {
   const int P = vggt3::ttt_num_chunks(a.n, a.H, tile_tokens(a.dt));
   if (P_out) *P_out = P;
   if (a.n == 0) return 0;
-  const size_t part = (size_t)a.H * P * 3 * a.d * a.m * sizeof(float);
-  const size_t loss = (size_t)a.H * P * sizeof(float);
-  return ((part + 255) / 256) * 256 + ((loss + 255) / 256) * 256;
+  return ws_layout(a, P).total;
+}
+
+bool valid_loss(int32_t loss) { return loss == VGGT3_LOSS_MSE || loss == VGGT3_LOSS_DOT; }
+
+hipError_t launch_partials(const void* K, const void* Vp, const float* theta, const MlpArgs& a, void* ws, int P,
+                           int32_t loss, hipStream_t s) {
+  const WsLayout l = ws_layout(a, P);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.part);
+  float* loss_part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.loss);
+  const bool dot = loss == VGGT3_LOSS_DOT;
+  if (a.dt == VGGT3_BF16) return vggt3::launch_grad_partial_bf16(K, Vp, theta, part, loss_part, a.n, a.H, P, dot, s);
+  return vggt3::launch_grad_partial_f32(K, Vp, theta, part, loss_part, a.n, a.H, a.d, a.m, P, dot, s);
 }
 
 // Gradient over all tokens into (part, loss_part) then reduce in `mode`.
-int run_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& a, void* ws, int P,
+int run_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& a, void* ws, int P, int32_t loss,
              vggt3::ReduceMode mode, float* dst, float lr, float* loss_out, hipStream_t s) {
-  float* part = static_cast<float*>(ws);
-  const size_t part_bytes = ((size_t)a.H * P * 3 * a.d * a.m * sizeof(float) + 255) / 256 * 256;
-  float* loss_part = reinterpret_cast<float*>(static_cast<char*>(ws) + part_bytes);
-  hipError_t e;
-  if (a.dt == VGGT3_BF16)
-    e = vggt3::launch_grad_partial_bf16(K, Vp, theta, part, loss_part, a.n, a.H, P, s);
-  else
-    e = vggt3::launch_grad_partial_f32(K, Vp, theta, part, loss_part, a.n, a.H, a.d, a.m, P, s);
-  int rc = check_hip(e, "gradient kernel launch");
+  int rc = check_hip(launch_partials(K, Vp, theta, a, ws, P, loss, s), "gradient kernel launch");
   if (rc) return rc;
+  const WsLayout l = ws_layout(a, P);
+  const float* part = reinterpret_cast<const float*>(static_cast<const char*>(ws) + l.part);
+  const float* loss_part = reinterpret_cast<const float*>(static_cast<const char*>(ws) + l.loss);
   return check_hip(vggt3::launch_reduce(part, loss_part, a.H, P, 3 * a.d * a.m, mode, dst, lr, loss_out, s),
                    "reduction kernel launch");
 }
@@ -160,12 +181,18 @@ size_t vggt3_ttt_workspace_bytes(int64_t n_tokens, int32_t n_heads, int32_t d_he
   return workspace_bytes(a, nullptr);
 }
 
-int vggt3_ttt_write(const void* K, const void* Vp, float* theta, int64_t n_tokens, int32_t n_heads, int32_t d_head,
-                    int32_t d_hidden, float lr, int32_t steps, int32_t dtype, void* workspace,
-                    size_t workspace_bytes_, float* loss_out, void* stream) {
+int vggt3_ttt_write_ex(const void* K, const void* Vp, float* theta, int64_t n_tokens, int32_t n_heads,
+                       int32_t d_head, int32_t d_hidden, float lr, int32_t steps, int32_t loss, int32_t optimizer,
+                       int32_t ns_steps, int32_t dtype, void* workspace, size_t workspace_bytes_, float* loss_out,
+                       void* stream) {
   const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
   int rc = check_mlp(a);
   if (rc) return rc;
+  if (!valid_loss(loss)) return fail(VGGT3_EINVAL, "unknown loss %d", loss);
+  if (optimizer != VGGT3_OPT_GD && optimizer != VGGT3_OPT_MUON)
+    return fail(VGGT3_EINVAL, "unknown optimizer %d", optimizer);
+  if (optimizer == VGGT3_OPT_MUON && (ns_steps < 0 || ns_steps > VGGT3_MAX_NS_STEPS))
+    return fail(VGGT3_EINVAL, "ns_steps = %d outside [0, %d]", ns_steps, VGGT3_MAX_NS_STEPS);
   if (!std::isfinite(lr)) return fail(VGGT3_EINVAL, "lr is not finite");
   if (steps < 1) return fail(VGGT3_EINVAL, "steps = %d < 1", steps);
   if (theta == nullptr) return fail(VGGT3_EINVAL, "theta is NULL");
@@ -194,20 +221,35 @@ int vggt3_ttt_write(const void* K, const void* Vp, float* theta, int64_t n_token
     }
     return ok();
   }
+  float* gbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_layout(a, P).grad);
   for (int st = 0; st < steps; ++st) {
-    rc = run_grad(K, Vp, theta, a, workspace, P, vggt3::kApply, theta, lr,
-                  loss_out ? loss_out + (size_t)st * n_heads : nullptr, s);
+    float* lrow = loss_out ? loss_out + (size_t)st * n_heads : nullptr;
+    if (optimizer == VGGT3_OPT_GD) {
+      rc = run_grad(K, Vp, theta, a, workspace, P, loss, vggt3::kApply, theta, lr, lrow, s);
+    } else {
+      rc = run_grad(K, Vp, theta, a, workspace, P, loss, vggt3::kStore, gbuf, 0.0f, lrow, s);
+      if (!rc)
+        rc = check_hip(vggt3::launch_muon_apply(theta, gbuf, lr, a.H, a.d, a.m, ns_steps, s), "muon launch");
+    }
     if (rc) return rc;
   }
   return ok();
 }
 
-int vggt3_ttt_grad(const void* K, const void* Vp, const float* theta, float* grad, int32_t accumulate,
-                   int64_t n_tokens, int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t dtype,
-                   void* workspace, size_t workspace_bytes_, float* loss_out, void* stream) {
+int vggt3_ttt_write(const void* K, const void* Vp, float* theta, int64_t n_tokens, int32_t n_heads, int32_t d_head,
+                    int32_t d_hidden, float lr, int32_t steps, int32_t dtype, void* workspace,
+                    size_t workspace_bytes_, float* loss_out, void* stream) {
+  return vggt3_ttt_write_ex(K, Vp, theta, n_tokens, n_heads, d_head, d_hidden, lr, steps, VGGT3_LOSS_MSE,
+                            VGGT3_OPT_GD, 0, dtype, workspace, workspace_bytes_, loss_out, stream);
+}
+
+int vggt3_ttt_grad_ex(const void* K, const void* Vp, const float* theta, float* grad, int32_t accumulate,
+                      int64_t n_tokens, int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t loss,
+                      int32_t dtype, void* workspace, size_t workspace_bytes_, float* loss_out, void* stream) {
   const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
   int rc = check_mlp(a);
   if (rc) return rc;
+  if (!valid_loss(loss)) return fail(VGGT3_EINVAL, "unknown loss %d", loss);
   if (theta == nullptr || grad == nullptr) return fail(VGGT3_EINVAL, "theta or grad is NULL");
   if (!aligned16(theta) || !aligned16(grad) || (loss_out && !aligned16(loss_out)))
     return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
@@ -234,17 +276,25 @@ int vggt3_ttt_grad(const void* K, const void* Vp, const float* theta, float* gra
     }
     return ok();
   }
-  rc = run_grad(K, Vp, theta, a, workspace, P, accumulate ? vggt3::kAccum : vggt3::kStore, grad, 0.0f, loss_out,
-                s);
+  rc = run_grad(K, Vp, theta, a, workspace, P, loss, accumulate ? vggt3::kAccum : vggt3::kStore, grad, 0.0f,
+                loss_out, s);
   return rc ? rc : ok();
 }
 
-int vggt3_ttt_grad_partials(const void* K, const void* Vp, const float* theta, int64_t n_tokens, int32_t n_heads,
-                            int32_t d_head, int32_t d_hidden, int32_t dtype, void* workspace,
-                            size_t workspace_bytes_, void* stream) {
+int vggt3_ttt_grad(const void* K, const void* Vp, const float* theta, float* grad, int32_t accumulate,
+                   int64_t n_tokens, int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t dtype,
+                   void* workspace, size_t workspace_bytes_, float* loss_out, void* stream) {
+  return vggt3_ttt_grad_ex(K, Vp, theta, grad, accumulate, n_tokens, n_heads, d_head, d_hidden, VGGT3_LOSS_MSE,
+                           dtype, workspace, workspace_bytes_, loss_out, stream);
+}
+
+int vggt3_ttt_grad_partials_ex(const void* K, const void* Vp, const float* theta, int64_t n_tokens,
+                               int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t loss, int32_t dtype,
+                               void* workspace, size_t workspace_bytes_, void* stream) {
   const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
   int rc = check_mlp(a);
   if (rc) return rc;
+  if (!valid_loss(loss)) return fail(VGGT3_EINVAL, "unknown loss %d", loss);
   if (theta == nullptr) return fail(VGGT3_EINVAL, "theta is NULL");
   if (!aligned16(theta)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
   if (a.n == 0) return ok();
@@ -257,15 +307,16 @@ int vggt3_ttt_grad_partials(const void* K, const void* Vp, const float* theta, i
   if (overlap(workspace, workspace_bytes_, theta, tb) || overlap(workspace, workspace_bytes_, K, xb) ||
       overlap(workspace, workspace_bytes_, Vp, xb))
     return fail(VGGT3_EINVAL, "workspace overlaps another argument");
-  float* part = static_cast<float*>(workspace);
-  const size_t part_bytes = ((size_t)a.H * P * 3 * a.d * a.m * sizeof(float) + 255) / 256 * 256;
-  float* loss_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_bytes);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = a.dt == VGGT3_BF16
-                     ? vggt3::launch_grad_partial_bf16(K, Vp, theta, part, loss_part, a.n, a.H, P, s)
-                     : vggt3::launch_grad_partial_f32(K, Vp, theta, part, loss_part, a.n, a.H, a.d, a.m, P, s);
-  rc = check_hip(e, "gradient kernel launch");
+  rc = check_hip(launch_partials(K, Vp, theta, a, workspace, P, loss, static_cast<hipStream_t>(stream)),
+                 "gradient kernel launch");
   return rc ? rc : ok();
+}
+
+int vggt3_ttt_grad_partials(const void* K, const void* Vp, const float* theta, int64_t n_tokens, int32_t n_heads,
+                            int32_t d_head, int32_t d_hidden, int32_t dtype, void* workspace,
+                            size_t workspace_bytes_, void* stream) {
+  return vggt3_ttt_grad_partials_ex(K, Vp, theta, n_tokens, n_heads, d_head, d_hidden, VGGT3_LOSS_MSE, dtype,
+                                    workspace, workspace_bytes_, stream);
 }
 
 int vggt3_ttt_reduce(const void* workspace, size_t workspace_bytes_, int64_t n_tokens, int32_t n_heads,
@@ -296,14 +347,33 @@ int vggt3_ttt_reduce(const void* workspace, size_t workspace_bytes_, int64_t n_t
   if (overlap(dst, tb, workspace, workspace_bytes_) || overlap(loss_out, lb, workspace, workspace_bytes_) ||
       overlap(dst, tb, loss_out, lb))
     return fail(VGGT3_EINVAL, "dst or loss_out overlaps another argument");
-  const float* part = static_cast<const float*>(workspace);
-  const size_t part_bytes = ((size_t)a.H * P * 3 * a.d * a.m * sizeof(float) + 255) / 256 * 256;
-  const float* loss_part = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + part_bytes);
+  const WsLayout l = ws_layout(a, P);
+  const float* part = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + l.part);
+  const float* loss_part = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + l.loss);
   const vggt3::ReduceMode rm = mode == VGGT3_REDUCE_APPLY   ? vggt3::kApply
                                : mode == VGGT3_REDUCE_STORE ? vggt3::kStore
                                                             : vggt3::kAccum;
   rc = check_hip(vggt3::launch_reduce(part, loss_part, a.H, P, 3 * a.d * a.m, rm, dst, lr, loss_out, s),
                  "reduction kernel launch");
+  return rc ? rc : ok();
+}
+
+int vggt3_ttt_muon_apply(float* theta, const float* grad, float lr, int32_t n_heads, int32_t d_head,
+                         int32_t d_hidden, int32_t ns_steps, void* stream) {
+  if (n_heads < 0 || d_head < 1 || d_hidden < 1) return fail(VGGT3_EINVAL, "bad shape");
+  if (!((d_head == 64 && d_hidden == 128) || (d_head == 16 && d_hidden == 32)))
+    return fail(VGGT3_EUNSUPPORTED, "no Muon kernel for d_head = %d, d_hidden = %d", d_head, d_hidden);
+  if (ns_steps < 0 || ns_steps > VGGT3_MAX_NS_STEPS)
+    return fail(VGGT3_EINVAL, "ns_steps = %d outside [0, %d]", ns_steps, VGGT3_MAX_NS_STEPS);
+  if (!std::isfinite(lr)) return fail(VGGT3_EINVAL, "lr is not finite");
+  const int64_t count = (int64_t)n_heads * 3 * d_head * d_hidden;
+  if (count == 0) return ok();
+  if (theta == nullptr || grad == nullptr) return fail(VGGT3_EINVAL, "theta or grad is NULL");
+  if (!aligned16(theta) || !aligned16(grad)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  if (overlap(theta, count * 4, grad, count * 4)) return fail(VGGT3_EINVAL, "grad overlaps theta");
+  int rc = check_hip(vggt3::launch_muon_apply(theta, grad, lr, n_heads, d_head, d_hidden, ns_steps,
+                                              static_cast<hipStream_t>(stream)),
+                     "muon launch");
   return rc ? rc : ok();
 }
 

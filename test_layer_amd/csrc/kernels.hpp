@@ -29,13 +29,19 @@ hipError_t launch_shortconv(const void* V, void* Vp, const float* w, int64_t n_v
                             int grid_w, int n_special, int C, bool bf16, hipStream_t stream);
 
 // Per-(head, chunk) fp32 gradient and loss partials.
-// part: [n_heads][P][3*d*m], loss_part: [n_heads][P].
+// part: [n_heads][P][3*d*m], loss_part: [n_heads][P]. dot selects the
+// dot-product loss -sum T(k).v' instead of sum (1/d)||T(k) - v'||^2.
 hipError_t launch_grad_partial_bf16(const void* K, const void* Vp, const float* theta, float* part,
-                                    float* loss_part, int64_t n_tokens, int n_heads, int P,
+                                    float* loss_part, int64_t n_tokens, int n_heads, int P, bool dot,
                                     hipStream_t stream);
 hipError_t launch_grad_partial_f32(const void* K, const void* Vp, const float* theta, float* part,
                                    float* loss_part, int64_t n_tokens, int n_heads, int d, int m, int P,
-                                   hipStream_t stream);
+                                   bool dot, hipStream_t stream);
+
+// Muon update theta -= lr * NS(grad) for every per-head weight matrix, NS the
+// `ns_steps`-step quintic Newton-Schulz orthogonalisation (fp32).
+hipError_t launch_muon_apply(float* theta, const float* grad, float lr, int n_heads, int d, int m, int ns_steps,
+                             hipStream_t stream);
 
 // Fixed-tree reduction of the partials, then (mode) either
 //   kApply:   theta -= lr * g            (write step), loss_out[h] = loss

@@ -1,9 +1,10 @@
 // fp32 kernels of the TTT write (gradient partials) and read passes.
 //
 // Same mathematics as the bf16 MFMA path (fast-weight SwiGLU T(x) =
-// (silu(x W_g) * (x W_u)) W_d, loss sum_i (1/d)||T(k_i) - v'_i||^2, gradient
-// summed per token chunk as in Eq. 5 of the paper-graph summary "VGG-T3:
-// Offline Feed-Forward 3D Reconstruction at Scale", section 3.4), evaluated
+// (silu(x W_g) * (x W_u)) W_d, loss sum_i (1/d)||T(k_i) - v'_i||^2 or, with
+// DOT, -sum_i T(k_i) . v'_i ("The dot product loss"), gradient summed per
+// token chunk as in Eq. 5 of the paper-graph summary "VGG-T3: Offline
+// Feed-Forward 3D Reconstruction at Scale", section 3.4), evaluated
 // entirely in fp32 on the vector ALUs. This path serves the fp32 mode (tight
 // tolerances, small heads); it stages the head's weights and every per-tile
 // intermediate in LDS and lets each thread own a fixed set of outputs.
@@ -23,7 +24,7 @@ struct F32Cfg {
 
 __device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
-template <int D, int M>
+template <int D, int M, bool DOT>
 __global__ __launch_bounds__(256, 1) void grad_partial_f32_kernel(const float* __restrict__ K,
                                                                 const float* __restrict__ Vp,
                                                                 const float* __restrict__ theta,
@@ -88,9 +89,14 @@ __global__ __launch_bounds__(256, 1) void grad_partial_f32_kernel(const float* _
       const int t = i / D, o = i % D;
       float y = 0.0f;
       for (int j = 0; j < M; ++j) y = fmaf(Hs[t * M + j], Wd[j * D + o], y);
-      const float R = y - Vs[i];
-      loss = fmaf(R, R, loss);
-      dYs[i] = (2.0f / D) * R;
+      if (DOT) {  // L = -sum y . v', dL/dy = -v'
+        loss = fmaf(-y, Vs[i], loss);
+        dYs[i] = -Vs[i];
+      } else {
+        const float R = y - Vs[i];
+        loss = fmaf(R, R, loss);
+        dYs[i] = (2.0f / D) * R;
+      }
     }
     __syncthreads();
     for (int i = tid; i < TT * M; i += 256) {
@@ -130,7 +136,8 @@ __global__ __launch_bounds__(256, 1) void grad_partial_f32_kernel(const float* _
   for (int off = 32; off >= 1; off >>= 1) loss += __shfl_xor(loss, off, 64);
   if ((tid & 63) == 0) red[tid >> 6] = loss;
   __syncthreads();
-  if (tid == 0) loss_part[(int64_t)head * P + chunk] = ((red[0] + red[1]) + (red[2] + red[3])) * (1.0f / D);
+  if (tid == 0)
+    loss_part[(int64_t)head * P + chunk] = ((red[0] + red[1]) + (red[2] + red[3])) * (DOT ? 1.0f : 1.0f / D);
 }
 
 template <int D, int M>
@@ -186,10 +193,15 @@ __global__ __launch_bounds__(256) void read_f32_kernel(const float* __restrict__
 
 template <int D, int M>
 hipError_t launch_grad_f32_t(const float* K, const float* Vp, const float* theta, float* part,
-                             float* loss_part, int64_t n_tokens, int n_heads, int P, hipStream_t stream) {
+                             float* loss_part, int64_t n_tokens, int n_heads, int P, bool dot,
+                             hipStream_t stream) {
   const int64_t n_blocks = (int64_t)n_heads * P;
-  hipLaunchKernelGGL((grad_partial_f32_kernel<D, M>), dim3((unsigned)n_blocks), dim3(256), 0, stream, K, Vp,
-                     theta, part, loss_part, n_tokens, n_heads, P, n_blocks);
+  if (dot)
+    hipLaunchKernelGGL((grad_partial_f32_kernel<D, M, true>), dim3((unsigned)n_blocks), dim3(256), 0, stream, K,
+                       Vp, theta, part, loss_part, n_tokens, n_heads, P, n_blocks);
+  else
+    hipLaunchKernelGGL((grad_partial_f32_kernel<D, M, false>), dim3((unsigned)n_blocks), dim3(256), 0, stream, K,
+                       Vp, theta, part, loss_part, n_tokens, n_heads, P, n_blocks);
   return hipGetLastError();
 }
 
@@ -210,11 +222,13 @@ hipError_t launch_read_f32_t(const float* Q, const float* theta, float* O, int64
 
 hipError_t launch_grad_partial_f32(const void* K, const void* Vp, const float* theta, float* part,
                                    float* loss_part, int64_t n_tokens, int n_heads, int d, int m, int P,
-                                   hipStream_t stream) {
+                                   bool dot, hipStream_t stream) {
   const float* k = static_cast<const float*>(K);
   const float* v = static_cast<const float*>(Vp);
-  if (d == 16 && m == 32) return launch_grad_f32_t<16, 32>(k, v, theta, part, loss_part, n_tokens, n_heads, P, stream);
-  if (d == 64 && m == 128) return launch_grad_f32_t<64, 128>(k, v, theta, part, loss_part, n_tokens, n_heads, P, stream);
+  if (d == 16 && m == 32)
+    return launch_grad_f32_t<16, 32>(k, v, theta, part, loss_part, n_tokens, n_heads, P, dot, stream);
+  if (d == 64 && m == 128)
+    return launch_grad_f32_t<64, 128>(k, v, theta, part, loss_part, n_tokens, n_heads, P, dot, stream);
   return hipErrorInvalidValue;
 }
 

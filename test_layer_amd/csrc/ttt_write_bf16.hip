@@ -32,6 +32,10 @@
 //   B0 | G,U(c) ; SwiGLU(c) -> H ; stage K,V'(c+1), load c+2
 //   B1 | Y(c) = H W_d (16x16x32 MFMA tiles over all hidden units) ; loss ; Y -> LDS
 //   B2 | dH(c) = (Y - V') W_d^T ; dG, dU ; gW_d, gW_g, gW_u += tile c
+// With the dot-product loss L = -sum_i T(k_i) . v'_i ("The dot product loss",
+// same section), dL/dY = -V' does not depend on Y: the Y phase and its two
+// barriers drop out, dH = -V' W_d^T, gW_d += H^T (-V'), and the loss is
+// sum H * dH over the tile (= -sum Y . V').
 // The kernel is sized (about 50 KB of LDS, at most 256 registers per lane, all
 // of them architectural VGPRs, so MFMA results need no copies before VALU use)
 // so that two workgroups share a CU: while one waits at a barrier or on LDS,
@@ -96,6 +100,7 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+template <bool DOT>
 __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
     const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg, const float* __restrict__ theta,
     float* __restrict__ part, float* __restrict__ loss_part, int64_t n_tokens, int n_heads, int P,
@@ -243,21 +248,23 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       Hop[ks] = pack8(&Hf[8 * ks]);
-      const u32x4 hv = as_u32x4(Hop[ks]);
-      lu16* hp = lds + OFF_H + o_hst + 16 * ks;
-      lst8(hp, u32x2{hv[0], hv[1]});
-      lst8(hp + 8, u32x2{hv[2], hv[3]});
+      if (!DOT) {
+        const u32x4 hv = as_u32x4(Hop[ks]);
+        lu16* hp = lds + OFF_H + o_hst + 16 * ks;
+        lst8(hp, u32x2{hv[0], hv[1]});
+        lst8(hp + 8, u32x2{hv[2], hv[3]});
+      }
     }
     // Stage tile i+1 (loaded during the previous tile) and start loading i+2.
     if (i + 1 < nt) {
       store_tile(i + 1);
       if (i + 2 < nt) load_tile(i + 2);
     }
-    __syncthreads();  // B1: H(i) complete
+    if (!DOT) __syncthreads();  // B1: H(i) complete
 
     // Y (tokens 16tb.., outputs 16(ob+b)..) = H W_d over all hidden units;
     // R = Y - V'; Y -> LDS [t][o].
-    {
+    if (!DOT) {
       f32x4 accY[2] = {f32x4{}, f32x4{}};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -289,17 +296,22 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
         yp[3 * TP] = (uint16_t)(y23 >> 16);
       }
     }
-    __syncthreads();  // B2: Y(i) complete
+    if (!DOT) __syncthreads();  // B2: Y(i) complete
 
-    // dH = (Y - V') W_d^T for this wave's hidden units; dU = dH A, dG = dH gp.
+    // dH = (Y - V') W_d^T (dot loss: -V' W_d^T) for this wave's hidden units;
+    // dU = dH A, dG = dH gp.
     bf16x8 dGop[2], dUop[2];
     {
       f32x16 accH = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 wdt = lop(lds + OFF_W + o_wrow + 16 * ks);  // B[k = o][j = hid]
-        accH = mfma32(lop(Yt + o_row + 16 * ks), wdt, accH);
+        if (!DOT) accH = mfma32(lop(Yt + o_row + 16 * ks), wdt, accH);
         accH = mfma32(lop(Vc + o_row + 16 * ks), wdt, accH);
+      }
+      if (DOT) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) loss = fmaf(Hf[r], accH[r], loss);
       }
       float dg[16], du[16];
 #pragma unroll
@@ -323,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
       for (int nb = 0; nb < 2; ++nb) {
         const lu16* yt = Yt + o_tr + 16 * ks * TP + 32 * nb;
         const lu16* vt = Vc + o_tr + 16 * ks * TP + 32 * nb;
-        accWd[nb] = mfma32(Hop[ks], ltr_op(yt, yt + 8 * TP), accWd[nb]);
+        if (!DOT) accWd[nb] = mfma32(Hop[ks], ltr_op(yt, yt + 8 * TP), accWd[nb]);
         accWd[nb] = mfma32(Hop[ks], ltr_op(vt, vt + 8 * TP), accWd[nb]);
       }
 #pragma unroll
@@ -336,8 +348,8 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
     }
   }
 
-  // Partials in theta layout, times 2/d.
-  constexpr float kScale = 2.0f / D;
+  // Partials in theta layout, times 2/d (mean squared error) or 1 (dot loss).
+  constexpr float kScale = DOT ? 1.0f : 2.0f / D;
   float* out = part + ((int64_t)head * P + chunk) * PER_HEAD;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -357,18 +369,23 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
   if (lane == 0) red[w] = loss;
   __syncthreads();
   if (tid == 0)
-    loss_part[(int64_t)head * P + chunk] = ((red[0] + red[1]) + (red[2] + red[3])) * (1.0f / D);
+    loss_part[(int64_t)head * P + chunk] = ((red[0] + red[1]) + (red[2] + red[3])) * (DOT ? 1.0f : 1.0f / D);
 }
 
 }  // namespace
 
 hipError_t launch_grad_partial_bf16(const void* K, const void* Vp, const float* theta, float* part,
-                                    float* loss_part, int64_t n_tokens, int n_heads, int P,
+                                    float* loss_part, int64_t n_tokens, int n_heads, int P, bool dot,
                                     hipStream_t stream) {
   const int64_t n_blocks = (int64_t)n_heads * P;
-  hipLaunchKernelGGL(grad_partial_bf16_kernel, dim3((unsigned)n_blocks), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(Vp), theta, part,
-                     loss_part, n_tokens, n_heads, P, n_blocks);
+  if (dot)
+    hipLaunchKernelGGL(grad_partial_bf16_kernel<true>, dim3((unsigned)n_blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(Vp), theta, part,
+                       loss_part, n_tokens, n_heads, P, n_blocks);
+  else
+    hipLaunchKernelGGL(grad_partial_bf16_kernel<false>, dim3((unsigned)n_blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(Vp), theta, part,
+                       loss_part, n_tokens, n_heads, P, n_blocks);
   return hipGetLastError();
 }
 

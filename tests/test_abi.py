@@ -145,3 +145,29 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, flags=re.M), f
+
+
+def test_recipe_entry_points_validate(lib):
+    n, H, d, m = 4096, 16, 64, 128
+    ws_need = lib.vggt3_ttt_workspace_bytes(n, H, d, m, tla.BF16)
+    big = ctypes.c_void_p(0x7000000000)
+
+    def write_ex(loss=0, opt=1, ns=5, dt=tla.BF16, lr=0.1):
+        return lib.vggt3_ttt_write_ex(FAKE, FAKE2, FAKE3, n, H, d, m, lr, 2, loss, opt, ns, dt, big, ws_need,
+                                      None, None)
+
+    assert write_ex(loss=2) == tla.EINVAL and "loss" in _err(lib)
+    assert write_ex(opt=7) == tla.EINVAL and "optimizer" in _err(lib)
+    assert write_ex(ns=-1) == tla.EINVAL and "ns_steps" in _err(lib)
+    assert write_ex(ns=65) == tla.EINVAL
+    assert write_ex(lr=float("nan")) == tla.EINVAL
+    assert lib.vggt3_ttt_grad_ex(FAKE, FAKE2, FAKE3, big, 0, n, H, d, m, 3, tla.BF16, big, ws_need, None,
+                                 None) == tla.EINVAL
+    assert lib.vggt3_ttt_grad_partials_ex(FAKE, FAKE2, FAKE3, n, H, d, m, -1, tla.BF16, big, ws_need,
+                                          None) == tla.EINVAL
+    # Muon apply: unsupported shape, bad step count, aliasing, empty
+    assert lib.vggt3_ttt_muon_apply(FAKE, FAKE2, 0.1, H, 32, 64, 5, None) == tla.EUNSUPPORTED
+    assert lib.vggt3_ttt_muon_apply(FAKE, FAKE2, 0.1, H, d, m, 99, None) == tla.EINVAL
+    assert lib.vggt3_ttt_muon_apply(FAKE, FAKE, 0.1, H, d, m, 5, None) == tla.EINVAL and "overlap" in _err(lib)
+    assert lib.vggt3_ttt_muon_apply(FAKE, None, 0.1, H, d, m, 5, None) == tla.EINVAL
+    assert lib.vggt3_ttt_muon_apply(FAKE, FAKE2, 0.1, 0, d, m, 5, None) == tla.OK
