@@ -146,3 +146,45 @@ def test_full_scene_sampled(name):
     # the scene's theta* read on the sample is consistent with per-token reads
     Os = tla.ttt_read(Qs.contiguous(), theta_w, cfg.n_heads)
     np.testing.assert_array_equal(bits(Os), bits(O.index_select(0, rt)))
+
+
+def test_views1000_pages_recipe_sampled():
+    """1000 views with the pages' recipe (dot-product loss, Muon), as
+    `bench.py --recipe dot_muon` times it. Checked: the dot-loss gradient of one
+    sampled head over all tokens at theta0, and that head's first Muon step
+    against the oracle's (bar 2e-2 times the oracle-measured Newton-Schulz
+    error gain, see tests/test_gpu_recipe.py); the fused write equals the
+    gradient + Muon-apply sequence bit for bit."""
+    from tests.test_gpu_recipe import _ns_gain
+    cfg = CONFIGS["views1000"]
+    n = cfg.n_tokens
+    print(f"[views1000 dot+muon] n={n}", flush=True)
+    inp = make_inputs(cfg, DEV, with_q=False)
+    Vp = tla.shortconv(inp.V, inp.conv_w, cfg.n_views, cfg.grid_h, cfg.grid_w, cfg.n_special)
+    ws = tla.make_workspace(n, cfg.n_heads, cfg.d_head, cfg.d_hidden, tla.BF16)
+    theta = inp.theta0.clone()
+    g0 = tla.ttt_grad(inp.K, Vp, theta, cfg.n_heads, workspace=ws, loss="dot")
+    tla.ttt_muon_apply(theta, g0, cfg.lr, cfg.n_heads, cfg.d_head, cfg.d_hidden, 5)
+    theta1 = theta.clone()
+    g1 = tla.ttt_grad(inp.K, Vp, theta, cfg.n_heads, workspace=ws, loss="dot")
+    tla.ttt_muon_apply(theta, g1, cfg.lr, cfg.n_heads, cfg.d_head, cfg.d_hidden, 5)
+    theta_w = inp.theta0.clone()
+    tla.ttt_write(inp.K, Vp, theta_w, cfg.lr, cfg.steps, cfg.n_heads, workspace=ws, loss="dot", optimizer="muon")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(theta_w), bits(theta))
+    print("  gpu done", flush=True)
+
+    h = 5
+    cols = slice(h * cfg.d_head, (h + 1) * cfg.d_head)
+    Kh = to64(inp.K[:, cols])
+    Vp_h = oracle.shortconv(inp.V[:, cols].to(torch.float32).cpu().numpy(), inp.conv_w[cols].cpu().numpy(),
+                            cfg.n_views, cfg.grid_h, cfg.grid_w, cfg.n_special, out="bf16").astype(np.float64)
+    th0 = inp.theta0.cpu().numpy()[h:h + 1]
+    g_ref, _ = oracle.ttt_grad(Kh, Vp_h, th0, 1, cfg.d_head, cfg.d_hidden, chunk=1 << 17, loss="dot")
+    e0 = rel_err(g0[h].cpu().numpy().astype(np.float64), g_ref[0])
+    th1_ref = oracle.muon_apply(th0, g_ref, cfg.lr, 1, cfg.d_head, cfg.d_hidden, 5)
+    kappa = _ns_gain(g_ref, 1, cfg.d_head, cfg.d_hidden)
+    d1 = rel_err(theta1[h].cpu().numpy().astype(np.float64) - th0[0], th1_ref[0] - th0[0])
+    print(f"  dot grad head {h}: rel err {e0:.3e}; Muon step: {d1:.3e} (NS gain {kappa:.2f})", flush=True)
+    assert e0 <= TOL_BF16
+    assert d1 <= TOL_BF16 * kappa
