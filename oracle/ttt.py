@@ -78,33 +78,38 @@ def shortconv(V, w, n_views: int, grid_h: int, grid_w: int, n_special: int,
     """V' = ShortConv2D(V) under the float32 conv contract.
 
     Each view's patch tokens are reshaped to a (grid_h, grid_w, C) grid, every
-    channel c is cross-correlated with its own 3x3 filter w[c] (zero padding,
+    channel c is cross-correlated with its own k x k filter w[c] (k odd: 3 is
+    the pages' ShortConv2D, 5 their "V-5" variant of Table 9; zero padding,
     same size) and the grid is flattened back; the view's special tokens are
     copied unchanged.
 
-    Contract (fixes the result bit for bit): per output element the nine taps
+    Contract (fixes the result bit for bit): per output element the k*k taps
     are visited with the row offset outermost and the column offset innermost,
-    both from -1 to +1; starting from acc = +0.0f, each tap does
+    both from -k//2 to +k//2; starting from acc = +0.0f, each tap does
     acc = fl32(acc + fl32(w * v)) — a separately rounded float32 product and
     sum, never a fused multiply-add; taps outside the grid see v = 0. With
     ``out="bf16"`` the float32 result is rounded to bfloat16 (ties to even).
 
-    Args: V [n, C] (float32 or exactly-widened bf16 values), w [C, 3, 3] float32.
+    Args: V [n, C] (float32 or exactly-widened bf16 values), w [C, k, k] float32.
     Returns float32 [n, C] (bf16-representable values when out == "bf16").
     """
     V32 = np.asarray(V, dtype=np.float32)
     w32 = np.asarray(w, dtype=np.float32)
     n, C = V32.shape
+    k = w32.shape[1]
+    if w32.shape != (C, k, k) or k % 2 != 1:
+        raise ValueError(f"filters must be [C, k, k] with k odd, got {w32.shape}")
+    r = k // 2
     tpv = _check_layout(n, n_views, grid_h, grid_w, n_special)
     res = V32.copy()  # special tokens pass through untouched
     grid = V32.reshape(n_views, tpv, C)[:, n_special:, :].reshape(n_views, grid_h, grid_w, C)
-    padded = np.zeros((n_views, grid_h + 2, grid_w + 2, C), dtype=np.float32)
-    padded[:, 1:-1, 1:-1, :] = grid
+    padded = np.zeros((n_views, grid_h + 2 * r, grid_w + 2 * r, C), dtype=np.float32)
+    padded[:, r:r + grid_h, r:r + grid_w, :] = grid
     acc = np.zeros((n_views, grid_h, grid_w, C), dtype=np.float32)
-    for dy in (-1, 0, 1):
-        for dx in (-1, 0, 1):
-            tap = padded[:, 1 + dy:1 + dy + grid_h, 1 + dx:1 + dx + grid_w, :]
-            prod = (w32[:, dy + 1, dx + 1] * tap).astype(np.float32)  # fl32(w * v)
+    for dy in range(-r, r + 1):
+        for dx in range(-r, r + 1):
+            tap = padded[:, r + dy:r + dy + grid_h, r + dx:r + dx + grid_w, :]
+            prod = (w32[:, dy + r, dx + r] * tap).astype(np.float32)  # fl32(w * v)
             acc = (acc + prod).astype(np.float32)  # fl32(acc + p)
     if out == "bf16":
         acc = bf16_round(acc)
@@ -115,15 +120,17 @@ def shortconv(V, w, n_views: int, grid_h: int, grid_w: int, n_special: int,
 
 
 def shortconv_direct(V, w, n_views: int, grid_h: int, grid_w: int, n_special: int) -> np.ndarray:
-    """Brute-force depthwise 3x3 convolution in float64 with explicit loops.
+    """Brute-force depthwise k x k convolution in float64 with explicit loops.
 
-    Written straight from the definition V'[y, x, c] = sum_{a,b in {-1,0,1}}
-    w[c, a+1, b+1] * V[y+a, x+b, c] over taps inside the grid. Pure Python: tiny
-    inputs only. Used to pin ``shortconv``.
+    Written straight from the definition V'[y, x, c] = sum_{a,b in -r..r}
+    w[c, a+r, b+r] * V[y+a, x+b, c] (r = k//2) over taps inside the grid. Pure
+    Python: tiny inputs only. Used to pin ``shortconv``.
     """
     V64 = np.asarray(V, dtype=np.float64)
     w64 = np.asarray(w, dtype=np.float64)
     n, C = V64.shape
+    r = w64.shape[1] // 2
+    offs = range(-r, r + 1)
     tpv = _check_layout(n, n_views, grid_h, grid_w, n_special)
     res = V64.copy()
     for v in range(n_views):
@@ -132,11 +139,11 @@ def shortconv_direct(V, w, n_views: int, grid_h: int, grid_w: int, n_special: in
             for x in range(grid_w):
                 for c in range(C):
                     s = 0.0
-                    for a in (-1, 0, 1):
-                        for b in (-1, 0, 1):
+                    for a in offs:
+                        for b in offs:
                             yy, xx = y + a, x + b
                             if 0 <= yy < grid_h and 0 <= xx < grid_w:
-                                s += w64[c, a + 1, b + 1] * V64[base + yy * grid_w + xx, c]
+                                s += w64[c, a + r, b + r] * V64[base + yy * grid_w + xx, c]
                     res[base + y * grid_w + x, c] = s
     return res
 

@@ -131,3 +131,55 @@ def test_contract_rounding_order_matters():
     out = shortconv(V, w, n_views, gh, gw, ns, out="f32")
     ref64 = shortconv_direct(V[:gh * gw * 1], w, 1, gh, gw, ns).astype(np.float32)
     assert not np.array_equal(out[:gh * gw], ref64)
+
+
+# ---- k x k filters: the pages' V-5 variant of ShortConv2D (Table 9) --------
+
+
+@pytest.mark.parametrize("layout", [(2, 6, 7, 1), (1, 2, 3, 0), (2, 1, 1, 2)])
+def test_5x5_contract_matches_bruteforce(layout):
+    n_views, gh, gw, ns = layout
+    C = 4
+    V = _rand((n_views * (ns + gh * gw), C), 21)
+    w = _rand((C, 5, 5), 22, 1 / 5)
+    ref = shortconv_direct(V, w, n_views, gh, gw, ns)
+    out = shortconv(V, w, n_views, gh, gw, ns, out="f32")
+    assert np.abs(out - ref).max() <= 1e-6 * max(np.abs(ref).max(), 1e-30)
+
+
+def test_5x5_contract_matches_torch_conv2d():
+    n_views, gh, gw, ns, C = 2, 9, 8, 3, 6
+    tpv = ns + gh * gw
+    V = _rand((n_views * tpv, C), 23)
+    w = _rand((C, 5, 5), 24, 1 / 5)
+    grid = torch.from_numpy(V.astype(np.float64)).view(n_views, tpv, C)[:, ns:, :]
+    x = grid.reshape(n_views, gh, gw, C).permute(0, 3, 1, 2)
+    y = torch.nn.functional.conv2d(x, torch.from_numpy(w.astype(np.float64)).unsqueeze(1), padding=2, groups=C)
+    ref = y.permute(0, 2, 3, 1).reshape(n_views, gh * gw, C).numpy()
+    out = shortconv(V, w, n_views, gh, gw, ns, out="f32").reshape(n_views, tpv, C)[:, ns:, :]
+    assert np.abs(out - ref).max() <= 1e-6 * np.abs(ref).max()
+    np.testing.assert_array_equal(shortconv(V, w, n_views, gh, gw, ns, out="f32").reshape(n_views, tpv, C)[:, :ns],
+                                  V.reshape(n_views, tpv, C)[:, :ns])
+
+
+@pytest.mark.parametrize("dy,dx", [(0, 0), (-2, 0), (2, 1), (-1, -2), (2, 2)])
+def test_5x5_delta_and_shift_kernels(dy, dx):
+    n_views, gh, gw, ns, C = 2, 6, 5, 1, 3
+    tpv = ns + gh * gw
+    V = bf16_round(_rand((n_views * tpv, C), 25))
+    w = np.zeros((C, 5, 5), np.float32)
+    w[:, dy + 2, dx + 2] = 1.0
+    out = shortconv(V, w, n_views, gh, gw, ns, out="bf16").reshape(n_views, tpv, C)[:, ns:, :]
+    grid = V.reshape(n_views, tpv, C)[:, ns:, :].reshape(n_views, gh, gw, C)
+    exp = np.zeros_like(grid)
+    for y in range(gh):
+        for x in range(gw):
+            if 0 <= y + dy < gh and 0 <= x + dx < gw:
+                exp[:, y, x] = grid[:, y + dy, x + dx]
+    np.testing.assert_array_equal(out.reshape(n_views, gh, gw, C), exp)
+
+
+def test_filter_shape_is_checked():
+    V = _rand((4, 2), 26)
+    with pytest.raises(ValueError):
+        shortconv(V, _rand((2, 4, 4), 27), 1, 2, 2, 0)
