@@ -121,6 +121,8 @@ def main():
     ap.add_argument("--config", default="views1000")
     ap.add_argument("--recipe", default="mse_gd", choices=sorted(RECIPES),
                     help="inner loss and update rule (default: squared error + gradient descent)")
+    ap.add_argument("--conv-variant", default="v3", choices=["v3", "v5", "kv3"],
+                    help="ShortConv2D variant of the pages' Table 9: 3x3 on V (default), 5x5 on V, 3x3 on K and V")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (counter calibration)")
@@ -145,6 +147,16 @@ def main():
     n, H, d, m = cfg.n_tokens, cfg.n_heads, cfg.d_head, cfg.d_hidden
     dt_code = tla.BF16 if cfg.dtype == "bf16" else tla.F32
     Vp = torch.empty_like(inp.V)
+    conv_w = inp.conv_w
+    conv_k = None
+    Kp = inp.K
+    if args.conv_variant != "v3":
+        gen = torch.Generator(device="cpu").manual_seed(cfg.seed * 1_000_003 + 17)
+        if args.conv_variant == "v5":
+            conv_w = (torch.randn((cfg.channels, 5, 5), generator=gen) / 5).to(dev)
+        else:
+            conv_k = (torch.randn((cfg.channels, 3, 3), generator=gen) / 3).to(dev)
+            Kp = torch.empty_like(inp.K)
     O = torch.empty_like(inp.Q)
     theta = inp.theta0.clone()
     ws = tla.make_workspace(n, H, d, m, dt_code, dev)
@@ -156,13 +168,15 @@ def main():
         theta.copy_(inp.theta0)
         if ev:
             ev["c0"].record()
-        tla.shortconv(inp.V, inp.conv_w, cfg.n_views, cfg.grid_h, cfg.grid_w, cfg.n_special, out=Vp)
+        tla.shortconv(inp.V, conv_w, cfg.n_views, cfg.grid_h, cfg.grid_w, cfg.n_special, out=Vp)
+        if conv_k is not None:
+            tla.shortconv(inp.K, conv_k, cfg.n_views, cfg.grid_h, cfg.grid_w, cfg.n_special, out=Kp)
         if ev:
             ev["c1"].record()
         for s in range(cfg.steps):
             if ev:
                 ev["g"][s][0].record()
-            tla.ttt_grad_partials(inp.K, Vp, theta, H, ws, loss=loss_kind)
+            tla.ttt_grad_partials(Kp, Vp, theta, H, ws, loss=loss_kind)
             if ev:
                 ev["g"][s][1].record()
             if opt_kind == "gd":
@@ -205,7 +219,7 @@ def main():
     achieved = grad_flops / (grad_avg_ms * 1e-3) / 1e12
     mlp_frac = (fw * n * cfg.steps + fr * nq) / ((write_ms + read_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
     esz = 2 if cfg.dtype == "bf16" else 4
-    conv_bytes = 2 * n * H * d * esz
+    conv_bytes = 2 * n * H * d * esz * (2 if args.conv_variant == "kv3" else 1)
     read_bytes = 2 * nq * H * d * esz
 
     if args.calib_copy:
@@ -232,6 +246,7 @@ def main():
             "n_views": cfg.n_views, "tokens_per_view": cfg.tokens_per_view, "n_tokens": n,
             "n_heads": H, "d_head": d, "d_hidden": m, "write_steps": cfg.steps, "lr": cfg.lr,
             "read_tokens": nq, "parallelism": "single GPU", "recipe": f"{args.recipe}: {recipe_desc}",
+            "conv_variant": {"v3": "3x3 on V", "v5": "5x5 on V", "kv3": "3x3 on K and on V"}[args.conv_variant],
         },
         "roofline": {
             "bound": "mfma",

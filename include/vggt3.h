@@ -116,6 +116,19 @@ int vggt3_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, in
                     void* stream);
 
 /*
+ * vggt3_shortconv with a k x k filter, ksize 3 or 5 ([GRAPH] "Non-Linear
+ * Spatial Mixing via ShortConv2D", Appendix C Table 9: the "V-5" variant uses
+ * 5 x 5). w is float32 [channels][ksize][ksize]; w[c][a+r][b+r] (r = ksize/2)
+ * multiplies the value at row offset a, column offset b. The evaluation
+ * contract is the same with offsets -r..r (row outer, column inner). Other
+ * arguments, errors and limits as in vggt3_shortconv. (Table 9's "KV-3"
+ * variant is vggt3_shortconv applied to K as well, with its own filters.)
+ */
+int vggt3_shortconv_ex(const void* V, void* Vp, const float* w, int64_t n_views, int32_t grid_h,
+                       int32_t grid_w, int32_t n_special, int32_t channels, int32_t ksize,
+                       int32_t dtype, void* stream);
+
+/*
  * Bytes of device workspace vggt3_ttt_write / vggt3_ttt_grad (and their _ex
  * forms) need for this problem: per-chunk fp32 gradient and loss partials of
  * the Eq. 5 split, plus one reduced gradient for Muon steps. Returns 0 for an

@@ -72,14 +72,20 @@ def _call(name: str, *args) -> int:
 
 def shortconv(V: torch.Tensor, w: torch.Tensor, n_views: int, grid_h: int, grid_w: int, n_special: int,
               out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """V' = depthwise 3x3 ShortConv2D of each view's patch grid; special tokens copied."""
+    """V' = depthwise k x k ShortConv2D of each view's patch grid (k = w.shape[-1],
+    3 or 5); special tokens copied."""
     if out is None:
         out = torch.empty_like(V)
     _check_dev(V, w, out)
-    if w.dtype != torch.float32:
-        raise TypeError("conv weights are float32 [C, 3, 3]")
-    _call("vggt3_shortconv", _ptr(V), _ptr(out), _ptr(w), n_views, grid_h, grid_w, n_special, V.shape[1],
-          _dtype_code(V), _stream())
+    if w.dtype != torch.float32 or w.dim() != 3 or w.shape[1] != w.shape[2]:
+        raise TypeError("conv weights are float32 [C, k, k]")
+    k = int(w.shape[-1])
+    if k == 3:
+        _call("vggt3_shortconv", _ptr(V), _ptr(out), _ptr(w), n_views, grid_h, grid_w, n_special, V.shape[1],
+              _dtype_code(V), _stream())
+    else:
+        _call("vggt3_shortconv_ex", _ptr(V), _ptr(out), _ptr(w), n_views, grid_h, grid_w, n_special, V.shape[1], k,
+              _dtype_code(V), _stream())
     return out
 
 
@@ -220,9 +226,16 @@ def ttt_read(Q: torch.Tensor, theta: torch.Tensor, n_heads: int, d_hidden: Optio
 
 
 def ttt_layer(K, V, Q, theta, conv_w, n_views, grid_h, grid_w, n_special, n_heads, lr, steps,
-              workspace=None, loss_out=None, Vp=None, O=None, loss="mse", optimizer="gd", ns_steps=5):
-    """The whole layer: V' = ShortConv2D(V); write theta (in place); O = read(Q)."""
+              workspace=None, loss_out=None, Vp=None, O=None, loss="mse", optimizer="gd", ns_steps=5,
+              conv_k=None):
+    """The whole layer: V' = ShortConv2D(V); write theta (in place); O = read(Q).
+
+    conv_w may be [C, 3, 3] (the pages' ShortConv2D) or [C, 5, 5] (their "V-5"
+    variant); conv_k, if given, convolves the keys as well before the write
+    (their "KV-3" variant, with its own filters)."""
     Vp = shortconv(V, conv_w, n_views, grid_h, grid_w, n_special, out=Vp)
+    if conv_k is not None:
+        K = shortconv(K, conv_k, n_views, grid_h, grid_w, n_special)
     ttt_write(K, Vp, theta, lr, steps, n_heads, workspace=workspace, loss_out=loss_out, loss=loss,
               optimizer=optimizer, ns_steps=ns_steps)
     return ttt_read(Q, theta, n_heads, out=O), Vp

@@ -24,6 +24,8 @@ SIGNATURES = {
     "vggt3_last_error": (ctypes.c_char_p, []),
     "vggt3_shortconv": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_int, c_int, c_int, c_int, c_int,
                                 c_void_p]),
+    "vggt3_shortconv_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_int, c_int, c_int, c_int, c_int, c_int,
+                                   c_void_p]),
     "vggt3_ttt_workspace_bytes": (c_size, [c_i64, c_int, c_int, c_int, c_int]),
     "vggt3_ttt_write": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_int, c_int, c_int, c_float, c_int,
                                 c_int, c_void_p, c_size, c_void_p, c_void_p]),

@@ -149,8 +149,9 @@ const char* vggt3_status_str(int status) {
 
 const char* vggt3_last_error(void) { return g_last_error.c_str(); }
 
-int vggt3_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, int32_t grid_h, int32_t grid_w,
-                    int32_t n_special, int32_t channels, int32_t dtype, void* stream) {
+int vggt3_shortconv_ex(const void* V, void* Vp, const float* w, int64_t n_views, int32_t grid_h, int32_t grid_w,
+                       int32_t n_special, int32_t channels, int32_t ksize, int32_t dtype, void* stream) {
+  if (ksize != 3 && ksize != 5) return fail(VGGT3_EUNSUPPORTED, "filter size %d is not 3 or 5", ksize);
   if (!valid_dtype(dtype)) return fail(VGGT3_EINVAL, "dtype %d is not VGGT3_BF16 or VGGT3_F32", dtype);
   if (n_views < 0 || grid_h < 1 || grid_w < 1 || n_special < 0 || channels < 1)
     return fail(VGGT3_EINVAL, "bad layout: n_views %lld, grid %dx%d, n_special %d, channels %d",
@@ -167,11 +168,17 @@ int vggt3_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, in
   if (!aligned16(V) || !aligned16(Vp) || !aligned16(w)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
   const size_t bytes = (size_t)n_views * ((size_t)n_special + (size_t)grid_h * grid_w) * channels * elem_size(dtype);
   if (overlap(V, bytes, Vp, bytes)) return fail(VGGT3_EINVAL, "V' overlaps V (in-place conv is not supported)");
-  if (overlap(w, (size_t)channels * 9 * sizeof(float), Vp, bytes)) return fail(VGGT3_EINVAL, "V' overlaps w");
-  int rc = check_hip(vggt3::launch_shortconv(V, Vp, w, n_views, grid_h, grid_w, n_special, channels,
-                                             dtype == VGGT3_BF16, static_cast<hipStream_t>(stream)),
+  if (overlap(w, (size_t)channels * ksize * ksize * sizeof(float), Vp, bytes))
+    return fail(VGGT3_EINVAL, "V' overlaps w");
+  int rc = check_hip(vggt3::launch_shortconv_k(V, Vp, w, n_views, grid_h, grid_w, n_special, channels, ksize,
+                                               dtype == VGGT3_BF16, static_cast<hipStream_t>(stream)),
                      "shortconv launch");
   return rc ? rc : ok();
+}
+
+int vggt3_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, int32_t grid_h, int32_t grid_w,
+                    int32_t n_special, int32_t channels, int32_t dtype, void* stream) {
+  return vggt3_shortconv_ex(V, Vp, w, n_views, grid_h, grid_w, n_special, channels, 3, dtype, stream);
 }
 
 size_t vggt3_ttt_workspace_bytes(int64_t n_tokens, int32_t n_heads, int32_t d_head, int32_t d_hidden,

@@ -27,6 +27,9 @@ int ttt_num_chunks(int64_t n_tokens, int n_heads, int tile_tokens);
 int shortconv_max_grid_w();
 hipError_t launch_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, int grid_h,
                             int grid_w, int n_special, int C, bool bf16, hipStream_t stream);
+// Filter size ksize (3: the kernel above; 5: the k x k variant kernel).
+hipError_t launch_shortconv_k(const void* V, void* Vp, const float* w, int64_t n_views, int grid_h, int grid_w,
+                              int n_special, int C, int ksize, bool bf16, hipStream_t stream);
 
 // Per-(head, chunk) fp32 gradient and loss partials.
 // part: [n_heads][P][3*d*m], loss_part: [n_heads][P]. dot selects the

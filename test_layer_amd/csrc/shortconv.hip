@@ -190,7 +190,115 @@ __global__ __launch_bounds__(256) void shortconv_kernel(const char* __restrict__
   }
 }
 
+// Any odd k x k filter (the pages' "V-5" variant of Table 9 uses k = 5): the
+// same work items and contract (row offset outer, column offset inner, both
+// -k/2..k/2, separately rounded fp32 product and sum, out-of-grid taps
+// skipped). A thread owns SEGK output rows; it keeps its channel group's
+// k*k filters in registers, issues the loads of all SEGK + k - 1 input rows at
+// the k columns at once (clamped, in-grid addresses; taps outside the grid are
+// skipped by uniform branches), and widens each row's taps as it needs them.
+constexpr int SEGK = 4;
+
+template <bool BF16, int KS>
+__global__ __launch_bounds__(256) void shortconv_kxk_kernel(const char* __restrict__ V, char* __restrict__ Vp,
+                                                             const float* __restrict__ w, int64_t n_work,
+                                                             int grid_h, int grid_w, int n_special, int C,
+                                                             int n_seg, int n_cblk) {
+  using Tr = ConvTraits<BF16>;
+  typedef typename Tr::vec_t vec_t;
+  constexpr int VB = (int)sizeof(vec_t);
+  constexpr int R = KS / 2;
+  constexpr int NR = SEGK + KS - 1;  // input rows per segment
+  const int CG = C / 4;
+  const int64_t row_bytes = (int64_t)C * Tr::ESZ;
+  const int64_t tpv = (int64_t)n_special + (int64_t)grid_h * grid_w;
+  const int64_t grid_row = (int64_t)grid_w * row_bytes;
+  const int64_t stride = gridDim.x;
+  float wt[KS * KS][4];
+  int wt_cblk = -1;
+  for (int64_t wi = xcd_remap(blockIdx.x, stride); wi < n_work; wi += stride) {
+    const int cblk = (int)(wi % n_cblk);
+    int64_t rest = wi / n_cblk;
+    const int x = (int)(rest % grid_w);
+    rest /= grid_w;
+    const int seg = (int)(rest % n_seg);
+    const int64_t view = rest / n_seg;
+    const int cg = cblk * 256 + (int)threadIdx.x;
+    if (cg >= CG) continue;
+    const uint32_t lane = (uint32_t)cg * VB;
+    const char* vview = V + view * tpv * row_bytes;
+    char* oview = Vp + view * tpv * row_bytes;
+    if (x == 0 && seg == 0) {
+      for (int s = 0; s < n_special; ++s)
+        *reinterpret_cast<vec_t*>(oview + s * row_bytes + lane) =
+            *reinterpret_cast<const vec_t*>(vview + s * row_bytes + lane);
+    }
+    if (cblk != wt_cblk) {
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+        for (int t = 0; t < KS * KS; ++t) wt[t][ch] = w[(int64_t)(cg * 4 + ch) * KS * KS + t];
+      wt_cblk = cblk;
+    }
+    const char* in_col = vview + ((int64_t)n_special + x) * row_bytes;
+    char* out_col = oview + ((int64_t)n_special + x) * row_bytes;
+    const int y0 = seg * SEGK;
+    vec_t raw[NR][KS];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int y = y0 - R + k;
+      const int yc = y < 0 ? 0 : (y >= grid_h ? grid_h - 1 : y);
+      const char* p = in_col + (int64_t)yc * grid_row + lane;
+#pragma unroll
+      for (int b = 0; b < KS; ++b) {
+        const int xc = x + b - R < 0 ? -x : (x + b - R >= grid_w ? grid_w - 1 - x : b - R);
+        raw[k][b] = *reinterpret_cast<const vec_t*>(p + xc * row_bytes);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < SEGK; ++k) {
+      const int y = y0 + k;
+      if (y >= grid_h) break;
+      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int a = 0; a < KS; ++a) {
+        if (y + a - R < 0 || y + a - R >= grid_h) continue;
+#pragma unroll
+        for (int b = 0; b < KS; ++b) {
+          if (x + b - R < 0 || x + b - R >= grid_w) continue;
+          float v[4];
+          Tr::widen(raw[k + a][b], v);
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch) acc[ch] = acc[ch] + wt[a * KS + b][ch] * v[ch];
+        }
+      }
+      __builtin_nontemporal_store(Tr::narrow(acc), reinterpret_cast<vec_t*>(out_col + (int64_t)y * grid_row + lane));
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_shortconv_k(const void* V, void* Vp, const float* w, int64_t n_views, int grid_h, int grid_w,
+                              int n_special, int C, int ksize, bool bf16, hipStream_t stream) {
+  if (ksize == 3) return launch_shortconv(V, Vp, w, n_views, grid_h, grid_w, n_special, C, bf16, stream);
+  if (ksize != 5) return hipErrorInvalidValue;
+  const int n_seg = (grid_h + SEGK - 1) / SEGK;
+  const int n_cblk = (C / 4 + 255) / 256;
+  const int64_t n_work = n_views * grid_w * (int64_t)n_seg * n_cblk;
+  if (n_work == 0) return hipSuccess;
+  const int64_t max_grid = (int64_t)VGGT3_CONV_WG_PER_CU * 256;
+  const unsigned n_blocks = (unsigned)(n_work < max_grid ? n_work : max_grid);
+  if (bf16)
+    hipLaunchKernelGGL((shortconv_kxk_kernel<true, 5>), dim3(n_blocks), dim3(256), 0, stream,
+                       static_cast<const char*>(V), static_cast<char*>(Vp), w, n_work, grid_h, grid_w, n_special, C,
+                       n_seg, n_cblk);
+  else
+    hipLaunchKernelGGL((shortconv_kxk_kernel<false, 5>), dim3(n_blocks), dim3(256), 0, stream,
+                       static_cast<const char*>(V), static_cast<char*>(Vp), w, n_work, grid_h, grid_w, n_special, C,
+                       n_seg, n_cblk);
+  return hipGetLastError();
+}
 
 hipError_t launch_shortconv(const void* V, void* Vp, const float* w, int64_t n_views, int grid_h,
                             int grid_w, int n_special, int C, bool bf16, hipStream_t stream) {

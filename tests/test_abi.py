@@ -171,3 +171,15 @@ def test_recipe_entry_points_validate(lib):
     assert lib.vggt3_ttt_muon_apply(FAKE, FAKE, 0.1, H, d, m, 5, None) == tla.EINVAL and "overlap" in _err(lib)
     assert lib.vggt3_ttt_muon_apply(FAKE, None, 0.1, H, d, m, 5, None) == tla.EINVAL
     assert lib.vggt3_ttt_muon_apply(FAKE, FAKE2, 0.1, 0, d, m, 5, None) == tla.OK
+
+
+def test_shortconv_ex_validation(lib):
+    def call(k, dt=tla.BF16, C=1024):
+        return lib.vggt3_shortconv_ex(FAKE, FAKE2, FAKE3, 2, 37, 37, 5, C, k, dt, None)
+
+    assert call(4) == tla.EUNSUPPORTED and "filter size" in _err(lib)
+    assert call(7) == tla.EUNSUPPORTED
+    assert call(5, dt=9) == tla.EINVAL
+    assert call(5, C=12) == tla.EUNSUPPORTED
+    assert lib.vggt3_shortconv_ex(FAKE, FAKE, FAKE3, 2, 37, 37, 5, 1024, 5, tla.BF16, None) == tla.EINVAL
+    assert lib.vggt3_shortconv_ex(FAKE, FAKE2, FAKE3, 0, 37, 37, 5, 1024, 5, tla.BF16, None) == tla.OK
