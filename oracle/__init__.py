@@ -16,5 +16,5 @@ routines, invariants); none is "parity unpinned".
 from .ttt import (  # noqa: F401
     bf16_round, shortconv, shortconv_direct, split_theta, join_theta,
     swiglu_forward, head_grad, ttt_grad, ttt_apply, ttt_write, ttt_read, ttt_loss,
-    newton_schulz, muon_apply, NS_COEFFS,
+    newton_schulz, muon_apply, NS_COEFFS, ttt_write_offload,
 )

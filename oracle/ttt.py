@@ -363,6 +363,36 @@ def ttt_write(K, Vp, theta0, n_heads: int, d: int, m: int, lr: float, steps: int
     return theta, losses, grads
 
 
+
+def ttt_write_offload(K, Vp, theta0, n_heads: int, d: int, m: int, lr: float, steps: int, minibatch: int,
+                      act: str = "silu", loss: str = "mse", opt: str = "gd", ns_steps: int = 5):
+    """The single-GPU offload schedule of [GRAPH] "Large-Scale Inference
+    Strategies": per step, take the tokens one minibatch of `minibatch` tokens
+    at a time, compute that minibatch's gradient at the step's theta, add it to
+    a running sum, and after the last minibatch apply the summed gradient. By
+    Eq. 5 this equals ttt_write up to rounding. Returns (theta* [H, 3dm],
+    losses [steps, H]).
+    """
+    if minibatch < 1:
+        raise ValueError("minibatch must be >= 1")
+    theta = np.asarray(theta0, dtype=np.float64).reshape(n_heads, 3 * d * m).copy()
+    K, Vp = np.asarray(K), np.asarray(Vp)
+    n = K.shape[0]
+    losses = np.zeros((steps, n_heads))
+    for s in range(steps):
+        g_sum = np.zeros_like(theta)
+        for t0 in range(0, n, minibatch):
+            g, L = ttt_grad(K[t0:t0 + minibatch], Vp[t0:t0 + minibatch], theta, n_heads, d, m, act, loss=loss)
+            g_sum += g
+            losses[s] += L
+        if opt == "gd":
+            theta = ttt_apply(theta, g_sum, lr)
+        elif opt == "muon":
+            theta = muon_apply(theta, g_sum, lr, n_heads, d, m, ns_steps)
+        else:
+            raise ValueError(opt)
+    return theta, losses
+
 def ttt_read(Q, theta, n_heads: int, d: int, m: int, act: str = "silu") -> np.ndarray:
     """Read pass o_i = T_theta(q_i) per head (Eq. 4 of [GRAPH]); float64 [n, C]."""
     Q = np.asarray(Q)
