@@ -113,6 +113,76 @@ def cpu_baseline(inp, cfg, target_s=15.0, max_views=256, loss="mse", opt="gd"):
     }
 
 
+def offload_bench(tla, inp, Vp, cfg, args, loss_kind, opt_kind):
+    """Time the layer with its token tensors in host memory: per step the
+    streamed write (every write step re-streams K and V') and the streamed
+    read of Q into a host O. V' is precomputed (the conv is not streamed)."""
+    import torch
+
+    chunk = args.offload
+    n, H = cfg.n_tokens, cfg.n_heads
+
+    def pinned(t):
+        h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+        h.copy_(t)
+        return h
+
+    Kh, Vh, Qh = pinned(inp.K), pinned(Vp), pinned(inp.Q)
+    Oh = torch.empty(Qh.shape, dtype=Qh.dtype, pin_memory=True)
+    theta = inp.theta0.clone()
+    d, m = cfg.d_head, cfg.d_hidden
+    dt_code = tla.BF16 if cfg.dtype == "bf16" else tla.F32
+    ct = min(chunk, n)
+    stage = torch.empty(tla.stage_bytes(ct, H, d, dt_code), dtype=torch.uint8, device=theta.device)
+    ws = tla.make_workspace(ct, H, d, m, dt_code, theta.device)
+
+    def step():
+        theta.copy_(inp.theta0)
+        tla.ttt_write_streamed(Kh, Vh, theta, cfg.lr, cfg.steps, H, chunk, stage=stage, workspace=ws,
+                               loss=loss_kind, optimizer=opt_kind)
+        tla.ttt_read_streamed(Qh, theta, H, chunk, out=Oh, stage=stage)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k = max(1, min(args.steps, 3))
+    a.record()
+    for _ in range(k):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / k
+
+    # the link's own rate: one plain pinned host-to-device and device-to-host copy of 1 GiB
+    src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device=theta.device)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    a.record()
+    dst.copy_(src, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    h2d_gbps = (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9
+    a.record()
+    src.copy_(dst, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    d2h_gbps = (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9
+
+    xb = Kh.numel() * Kh.element_size()
+    qb = Qh.numel() * Qh.element_size()
+    h2d = cfg.steps * 2 * xb + qb if -(-n // ct) > 2 else 2 * xb + qb
+    d2h = qb
+    return {
+        "chunk_tokens": chunk, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3), "steps_timed": k,
+        "h2d_bytes_per_step": h2d, "d2h_bytes_per_step": d2h,
+        "pcie_GBps": (h2d + d2h) / (ms * 1e-3) / 1e9,
+        "copy_GBps": {"h2d": h2d_gbps, "d2h": d2h_gbps},
+        "note": "K, V' and Q in pinned host memory, O written to pinned host memory; V' precomputed",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +194,9 @@ def main():
     ap.add_argument("--conv-variant", default="v3", choices=["v3", "v5", "kv3"],
                     help="ShortConv2D variant of the pages' Table 9: 3x3 on V (default), 5x5 on V, 3x3 on K and V")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--offload", type=int, default=0, metavar="CHUNK",
+                    help="also time the offloaded step (K, V', Q in pinned host memory, streamed through the GPU in "
+                         "CHUNK-token chunks; O streamed back) and report it under 'offload' (never as value)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -264,6 +337,8 @@ def main():
         "hbm_GBps": {"conv": conv_bytes / (conv_ms * 1e-3) / 1e9, "read": read_bytes / (read_ms * 1e-3) / 1e9},
         "final_loss_head0": float(loss[-1, 0].item()),
     }
+    if args.offload > 0:
+        res["offload"] = offload_bench(tla, inp, Vp, cfg, args, loss_kind, opt_kind)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, cfg, loss=loss_kind, opt=opt_kind)
     print(json.dumps(res), flush=True)

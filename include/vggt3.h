@@ -25,7 +25,8 @@
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
- *     aligned. The library allocates no device memory and keeps no state
+ *     aligned (the streamed entry points at the end take HOST token tensors,
+ *     as they say). The library allocates no device memory and keeps no state
  *     between calls apart from a per-thread last-error string.
  *   - Token tensors (K, V, V', Q, O) are row-major [n_tokens][C] with
  *     C = n_heads * d_head; head h owns columns h*d_head .. h*d_head+d_head-1.
@@ -264,6 +265,78 @@ int vggt3_ttt_apply(float* theta, const float* grad, float lr, int32_t n_heads, 
  */
 int vggt3_ttt_read(const void* Q, const float* theta, void* O, int64_t n_tokens, int32_t n_heads,
                    int32_t d_head, int32_t d_hidden, int32_t dtype, void* stream);
+
+/*
+ * Streamed (offloaded) write and read: the scene's token tensors stay in HOST
+ * memory and pass through the GPU one chunk of tokens at a time ([GRAPH]
+ * "Large-Scale Inference Strategies", single-GPU CPU offloading: load a
+ * minibatch to the device, compute its gradient, accumulate, drop it, repeat,
+ * then apply the summed update; exact by Eq. 5. Query mode reads a frozen
+ * theta* the same way). Host-to-device copies of chunk c+1 run on a copy stream
+ * while chunk c is computed on `stream`, through two device staging slots.
+ *
+ * Host buffers should be pinned (allocated with hipHostMalloc or as pinned
+ * tensors) for the copies to run asynchronously; pageable memory gives the
+ * same results, with copies that do not overlap the kernels. The caller must
+ * not modify or free host inputs, or read host outputs, until `stream` has
+ * been synchronised: every copy and kernel of the call is ordered before work
+ * enqueued later on `stream`, and after work enqueued earlier on it.
+ *
+ * Bytes of device staging a streamed call needs for chunks of chunk_tokens
+ * tokens: two slots of two token tensors each (K and V' for the write, Q and O
+ * for the read). Returns 0 for chunk_tokens < 1 or an invalid shape.
+ */
+size_t vggt3_ttt_stream_stage_bytes(int64_t chunk_tokens, int32_t n_heads, int32_t d_head, int32_t dtype);
+
+/*
+ * vggt3_ttt_write_ex over host-resident K and V'. Each step streams all
+ * n_tokens tokens in chunks of chunk_tokens (the last chunk may be shorter):
+ * per chunk, the gradient is computed at the step's theta and added into an
+ * fp32 accumulator in the workspace; after the last chunk the step's update
+ * (VGGT3_OPT_GD or VGGT3_OPT_MUON) is applied. When the whole scene fits in
+ * the two staging slots (at most two chunks), it is copied once and reused by
+ * every step.
+ *
+ *   K_host, Vp_host  HOST [n_tokens][C], dtype; read only.
+ *   theta            DEVICE float32 [n_heads][3*d_head*d_hidden], updated.
+ *   chunk_tokens     >= 1; tokens per device-resident chunk.
+ *   stage            DEVICE, at least vggt3_ttt_stream_stage_bytes(
+ *                    min(chunk_tokens, n_tokens), ...) bytes.
+ *   workspace        DEVICE, at least vggt3_ttt_workspace_bytes(
+ *                    min(chunk_tokens, n_tokens), ...) bytes (sized for one
+ *                    chunk, not for the scene).
+ *   loss_out         NULL or DEVICE float32 [steps][n_heads].
+ *   stream           compute stream; copy_stream carries the host-to-device
+ *                    copies (NULL or equal to stream serialises them).
+ * theta, stage, workspace and loss_out must not overlap. The gradient equals
+ * vggt3_ttt_grad called with accumulate on each chunk in turn, bit for bit.
+ * Errors as in vggt3_ttt_write_ex; a HIP runtime error part-way through
+ * returns VGGT3_EHIP with part of the work enqueued.
+ */
+int vggt3_ttt_write_streamed(const void* K_host, const void* Vp_host, float* theta, int64_t n_tokens,
+                             int32_t n_heads, int32_t d_head, int32_t d_hidden, float lr, int32_t steps,
+                             int32_t loss, int32_t optimizer, int32_t ns_steps, int32_t dtype,
+                             int64_t chunk_tokens, void* stage, size_t stage_bytes, void* workspace,
+                             size_t workspace_bytes, float* loss_out, void* stream, void* copy_stream);
+
+/*
+ * vggt3_ttt_read over host-resident Q and O (query mode over a frozen theta*):
+ * chunk c+1 is copied in on h2d_stream and chunk c-1 copied out on d2h_stream
+ * while chunk c is read on `stream` (the two copy streams may be the same
+ * stream; NULL or `stream` serialises the copies with the kernels).
+ *
+ *   Q_host       HOST [n_tokens][C], dtype; read only.
+ *   theta        DEVICE float32 [n_heads][3*d_head*d_hidden]; read only.
+ *   O_host       HOST [n_tokens][C], dtype; written. Must not overlap Q_host.
+ *   stage        DEVICE, at least vggt3_ttt_stream_stage_bytes(
+ *                min(chunk_tokens, n_tokens), ...) bytes; must not overlap
+ *                theta.
+ * Output equals vggt3_ttt_read's bit for bit. n_tokens == 0 is a no-op.
+ */
+int vggt3_ttt_read_streamed(const void* Q_host, const float* theta, void* O_host, int64_t n_tokens,
+                            int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t dtype,
+                            int64_t chunk_tokens, void* stage, size_t stage_bytes, void* stream,
+                            void* h2d_stream, void* d2h_stream);
 
 #ifdef __cplusplus
 }

@@ -239,3 +239,91 @@ def ttt_layer(K, V, Q, theta, conv_w, n_views, grid_h, grid_w, n_special, n_head
     ttt_write(K, Vp, theta, lr, steps, n_heads, workspace=workspace, loss_out=loss_out, loss=loss,
               optimizer=optimizer, ns_steps=ns_steps)
     return ttt_read(Q, theta, n_heads, out=O), Vp
+
+
+# ---------------------------------------------------------------------------
+# Streamed (offloaded) write and read over host-resident token tensors
+# ---------------------------------------------------------------------------
+
+_side_streams = {}
+
+
+def _side_stream(device: torch.device, key: str) -> torch.cuda.Stream:
+    """A per-device copy stream of default priority, created once."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    s = _side_streams.get((idx, key))
+    if s is None:
+        s = torch.cuda.Stream(device=idx)
+        _side_streams[(idx, key)] = s
+    return s
+
+
+def _check_host(*ts):
+    for t in ts:
+        if t.is_cuda:
+            raise ValueError("streamed token tensors live in host memory (pinned for overlap)")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def stage_bytes(chunk_tokens: int, n_heads: int, d_head: int, dtype_code: int) -> int:
+    """Device staging a streamed call needs: two slots of two token chunks."""
+    return int(lib().vggt3_ttt_stream_stage_bytes(chunk_tokens, n_heads, d_head, dtype_code))
+
+
+def ttt_write_streamed(K_host: torch.Tensor, Vp_host: torch.Tensor, theta: torch.Tensor, lr: float, steps: int,
+                       n_heads: int, chunk_tokens: int, d_hidden: Optional[int] = None,
+                       stage: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       loss_out: Optional[torch.Tensor] = None, loss="mse", optimizer="gd", ns_steps: int = 5,
+                       copy_stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """ttt_write over host-resident K and V' streamed in chunks of `chunk_tokens`
+    (Eq. 5 offload schedule); theta is a device tensor updated in place.
+
+    The copies run on `copy_stream` (default: a side stream of this device)
+    while the kernels run on the current stream; the host tensors must stay
+    untouched until the current stream has been synchronised."""
+    _check_host(K_host, Vp_host)
+    _check_dev(theta, stage, workspace, loss_out)
+    d, m = _mlp_dims(theta, K_host, n_heads, d_hidden)
+    dt = _dtype_code(K_host)
+    n = K_host.shape[0]
+    ct = max(1, min(int(chunk_tokens), n))
+    if stage is None:
+        stage = torch.empty(stage_bytes(ct, n_heads, d, dt), dtype=torch.uint8, device=theta.device)
+    if workspace is None:
+        workspace = make_workspace(ct, n_heads, d, m, dt, theta.device)
+    if copy_stream is None:
+        copy_stream = _side_stream(theta.device, "h2d")
+    ws_nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("vggt3_ttt_write_streamed", _ptr(K_host), _ptr(Vp_host), _ptr(theta), n, n_heads, d, m, float(lr),
+          int(steps), _loss_code(loss), _opt_code(optimizer), int(ns_steps), dt, int(chunk_tokens), _ptr(stage),
+          stage.numel() * stage.element_size(), _ptr(workspace), ws_nb, _ptr(loss_out), _stream(),
+          ctypes.c_void_p(copy_stream.cuda_stream))
+    return theta
+
+
+def ttt_read_streamed(Q_host: torch.Tensor, theta: torch.Tensor, n_heads: int, chunk_tokens: int,
+                      d_hidden: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                      stage: Optional[torch.Tensor] = None, h2d_stream: Optional[torch.cuda.Stream] = None,
+                      d2h_stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """O = T_theta(Q) for host-resident Q, written to a host tensor (query mode
+    over a frozen theta), streamed in chunks of `chunk_tokens`. `out` defaults
+    to a new pinned tensor; read it after synchronising the current stream."""
+    if out is None:
+        out = torch.empty(Q_host.shape, dtype=Q_host.dtype, pin_memory=True)
+    _check_host(Q_host, out)
+    _check_dev(theta, stage)
+    d, m = _mlp_dims(theta, Q_host, n_heads, d_hidden)
+    dt = _dtype_code(Q_host)
+    n = Q_host.shape[0]
+    ct = max(1, min(int(chunk_tokens), n))
+    if stage is None:
+        stage = torch.empty(stage_bytes(ct, n_heads, d, dt), dtype=torch.uint8, device=theta.device)
+    if h2d_stream is None:
+        h2d_stream = _side_stream(theta.device, "h2d")
+    if d2h_stream is None:
+        d2h_stream = _side_stream(theta.device, "d2h")
+    _call("vggt3_ttt_read_streamed", _ptr(Q_host), _ptr(theta), _ptr(out), n, n_heads, d, m, dt, int(chunk_tokens),
+          _ptr(stage), stage.numel() * stage.element_size(), _stream(), ctypes.c_void_p(h2d_stream.cuda_stream),
+          ctypes.c_void_p(d2h_stream.cuda_stream))
+    return out

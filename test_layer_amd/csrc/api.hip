@@ -130,6 +130,29 @@ int check_workspace(const MlpArgs& a, const void* ws, size_t ws_bytes, int* P) {
   return VGGT3_OK;
 }
 
+// Events for one streamed call. Destroying an event whose recorded work is
+// still pending is allowed: the runtime releases it once that work completes.
+struct CallEvents {
+  static constexpr int kMax = 8;
+  hipEvent_t e[kMax] = {};
+  int n = 0;
+  hipError_t create(int count) {
+    for (; n < count && n < kMax; ++n) {
+      const hipError_t r = hipEventCreateWithFlags(&e[n], hipEventDisableTiming);
+      if (r != hipSuccess) return r;
+    }
+    return hipSuccess;
+  }
+  ~CallEvents() {
+    for (int i = 0; i < n; ++i) (void)hipEventDestroy(e[i]);
+  }
+};
+
+// One staging slot holds one chunk of one token tensor.
+size_t stage_slot_bytes(int64_t chunk_tokens, int32_t C, int32_t dt) {
+  return round256((size_t)chunk_tokens * C * elem_size(dt));
+}
+
 }  // namespace
 
 extern "C" {
@@ -412,6 +435,212 @@ int vggt3_ttt_read(const void* Q, const float* theta, void* O, int64_t n_tokens,
                                      : vggt3::launch_read_f32(Q, theta, O, a.n, a.H, a.d, a.m, s);
   rc = check_hip(e, "read kernel launch");
   return rc ? rc : ok();
+}
+
+size_t vggt3_ttt_stream_stage_bytes(int64_t chunk_tokens, int32_t n_heads, int32_t d_head, int32_t dtype) {
+  if (chunk_tokens < 1 || n_heads < 1 || d_head < 1 || !valid_dtype(dtype)) return 0;
+  if ((int64_t)n_heads * d_head > (int64_t)1 << 20) return 0;
+  return 4 * stage_slot_bytes(chunk_tokens, n_heads * d_head, dtype);
+}
+
+int vggt3_ttt_write_streamed(const void* K_host, const void* Vp_host, float* theta, int64_t n_tokens,
+                             int32_t n_heads, int32_t d_head, int32_t d_hidden, float lr, int32_t steps,
+                             int32_t loss, int32_t optimizer, int32_t ns_steps, int32_t dtype,
+                             int64_t chunk_tokens, void* stage, size_t stage_bytes, void* workspace,
+                             size_t workspace_bytes_, float* loss_out, void* stream, void* copy_stream) {
+  const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
+  int rc = check_mlp(a);
+  if (rc) return rc;
+  if (!valid_loss(loss)) return fail(VGGT3_EINVAL, "unknown loss %d", loss);
+  if (optimizer != VGGT3_OPT_GD && optimizer != VGGT3_OPT_MUON)
+    return fail(VGGT3_EINVAL, "unknown optimizer %d", optimizer);
+  if (optimizer == VGGT3_OPT_MUON && (ns_steps < 0 || ns_steps > VGGT3_MAX_NS_STEPS))
+    return fail(VGGT3_EINVAL, "ns_steps = %d outside [0, %d]", ns_steps, VGGT3_MAX_NS_STEPS);
+  if (optimizer == VGGT3_OPT_MUON && !((d_head == 64 && d_hidden == 128) || (d_head == 16 && d_hidden == 32)))
+    return fail(VGGT3_EUNSUPPORTED, "no Muon kernel for d_head = %d, d_hidden = %d", d_head, d_hidden);
+  if (!std::isfinite(lr)) return fail(VGGT3_EINVAL, "lr is not finite");
+  if (steps < 1) return fail(VGGT3_EINVAL, "steps = %d < 1", steps);
+  if (chunk_tokens < 1) return fail(VGGT3_EINVAL, "chunk_tokens = %lld < 1", (long long)chunk_tokens);
+  if (theta == nullptr) return fail(VGGT3_EINVAL, "theta is NULL");
+  if (!aligned16(theta) || (loss_out && !aligned16(loss_out)))
+    return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t lb = loss_out ? (size_t)steps * n_heads * sizeof(float) : 0;
+  if (overlap(theta, theta_bytes(a), loss_out, lb)) return fail(VGGT3_EINVAL, "loss_out overlaps theta");
+  if (a.n == 0) {
+    if (loss_out) {
+      rc = check_hip(vggt3::launch_fill(loss_out, 0.0f, (int64_t)steps * n_heads, s), "fill launch");
+      if (rc) return rc;
+    }
+    return ok();
+  }
+  if (K_host == nullptr || Vp_host == nullptr) return fail(VGGT3_EINVAL, "K or V' is NULL");
+  const int64_t ct = chunk_tokens < a.n ? chunk_tokens : a.n;
+  const MlpArgs ca{ct, n_heads, d_head, d_hidden, dtype};
+  int P = 1;
+  rc = check_workspace(ca, workspace, workspace_bytes_, &P);
+  if (rc) return rc;
+  const int32_t C = n_heads * d_head;
+  const size_t slot = stage_slot_bytes(ct, C, dtype), need = 4 * slot;
+  if (stage == nullptr) return fail(VGGT3_EINVAL, "stage is NULL");
+  if (stage_bytes < need) return fail(VGGT3_EWORKSPACE, "stage has %zu bytes, %zu needed", stage_bytes, need);
+  if (!aligned16(stage)) return fail(VGGT3_EINVAL, "stage is not 16-byte aligned");
+  const size_t tb = theta_bytes(a);
+  if (overlap(theta, tb, stage, stage_bytes) || overlap(theta, tb, workspace, workspace_bytes_))
+    return fail(VGGT3_EINVAL, "theta overlaps stage or workspace");
+  if (overlap(stage, stage_bytes, workspace, workspace_bytes_) || overlap(loss_out, lb, stage, stage_bytes) ||
+      overlap(loss_out, lb, workspace, workspace_bytes_))
+    return fail(VGGT3_EINVAL, "stage, workspace and loss_out overlap");
+
+  // The accumulated gradient sits where the workspace layout of a full chunk
+  // puts its reduced gradient; a shorter last chunk has no more partials
+  // (ttt_num_chunks grows with n), so its partials end before it.
+  float* gacc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_layout(ca, P).grad);
+  const int64_t nc = (a.n + ct - 1) / ct;
+  const int64_t tail = a.n - (nc - 1) * ct;
+  if (ws_layout(MlpArgs{tail, n_heads, d_head, d_hidden, dtype},
+                vggt3::ttt_num_chunks(tail, n_heads, tile_tokens(dtype)))
+          .grad > ws_layout(ca, P).grad)
+    return fail(VGGT3_EUNSUPPORTED, "internal: tail chunk layout exceeds the workspace");
+
+  hipStream_t cs = copy_stream ? static_cast<hipStream_t>(copy_stream) : s;
+  CallEvents ev;
+  rc = check_hip(ev.create(5), "event create");
+  if (rc) return rc;
+  hipEvent_t entry = ev.e[0], copied[2] = {ev.e[1], ev.e[2]}, freed[2] = {ev.e[3], ev.e[4]};
+  // Staging slots may still be read by earlier work on `stream`.
+  rc = check_hip(hipEventRecord(entry, s), "event record");
+  if (!rc && cs != s) rc = check_hip(hipStreamWaitEvent(cs, entry, 0), "stream wait");
+  if (rc) return rc;
+
+  const size_t row = (size_t)C * elem_size(dtype);
+  char* st = static_cast<char*>(stage);
+  const bool resident = nc <= 2;  // the whole scene fits in the two slots
+  int64_t use = 0;
+  for (int step = 0; step < steps; ++step) {
+    float* lrow = loss_out ? loss_out + (size_t)step * n_heads : nullptr;
+    for (int64_t c = 0; c < nc; ++c, ++use) {
+      const int sl = resident ? (int)c : (int)(use & 1);
+      const int64_t t0 = c * ct, tn = c + 1 < nc ? ct : tail;
+      void* Kd = st + (size_t)(2 * sl) * slot;
+      void* Vd = st + (size_t)(2 * sl + 1) * slot;
+      if (!resident || step == 0) {
+        // Refill slot sl once the chunk that last used it has been consumed.
+        if (use >= 2) rc = check_hip(hipStreamWaitEvent(cs, freed[sl], 0), "stream wait");
+        if (!rc)
+          rc = check_hip(hipMemcpyAsync(Kd, static_cast<const char*>(K_host) + (size_t)t0 * row, (size_t)tn * row,
+                                        hipMemcpyHostToDevice, cs),
+                         "K copy");
+        if (!rc)
+          rc = check_hip(hipMemcpyAsync(Vd, static_cast<const char*>(Vp_host) + (size_t)t0 * row, (size_t)tn * row,
+                                        hipMemcpyHostToDevice, cs),
+                         "V' copy");
+        if (!rc && cs != s) {
+          rc = check_hip(hipEventRecord(copied[sl], cs), "event record");
+          if (!rc) rc = check_hip(hipStreamWaitEvent(s, copied[sl], 0), "stream wait");
+        }
+        if (rc) return rc;
+      }
+      const MlpArgs ta{tn, n_heads, d_head, d_hidden, dtype};
+      rc = run_grad(Kd, Vd, theta, ta, workspace, vggt3::ttt_num_chunks(tn, n_heads, tile_tokens(dtype)), loss,
+                    c == 0 ? vggt3::kStore : vggt3::kAccum, gacc, 0.0f, lrow, s);
+      if (!rc && cs != s) rc = check_hip(hipEventRecord(freed[sl], s), "event record");
+      if (rc) return rc;
+    }
+    if (optimizer == VGGT3_OPT_GD)
+      rc = check_hip(vggt3::launch_apply(theta, gacc, lr, (int64_t)tb / 4, s), "apply launch");
+    else
+      rc = check_hip(vggt3::launch_muon_apply(theta, gacc, lr, n_heads, d_head, d_hidden, ns_steps, s),
+                     "muon launch");
+    if (rc) return rc;
+  }
+  return ok();
+}
+
+int vggt3_ttt_read_streamed(const void* Q_host, const float* theta, void* O_host, int64_t n_tokens,
+                            int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t dtype,
+                            int64_t chunk_tokens, void* stage, size_t stage_bytes, void* stream,
+                            void* h2d_stream, void* d2h_stream) {
+  const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
+  int rc = check_mlp(a);
+  if (rc) return rc;
+  if (chunk_tokens < 1) return fail(VGGT3_EINVAL, "chunk_tokens = %lld < 1", (long long)chunk_tokens);
+  if (a.n == 0) return ok();
+  if (Q_host == nullptr || theta == nullptr || O_host == nullptr) return fail(VGGT3_EINVAL, "NULL pointer");
+  if (!aligned16(theta)) return fail(VGGT3_EINVAL, "theta is not 16-byte aligned");
+  const size_t xb = token_bytes(a);
+  if (overlap(Q_host, xb, O_host, xb)) return fail(VGGT3_EINVAL, "O overlaps Q");
+  const int64_t ct = chunk_tokens < a.n ? chunk_tokens : a.n;
+  const int32_t C = n_heads * d_head;
+  const size_t slot = stage_slot_bytes(ct, C, dtype), need = 4 * slot;
+  if (stage == nullptr) return fail(VGGT3_EINVAL, "stage is NULL");
+  if (stage_bytes < need) return fail(VGGT3_EWORKSPACE, "stage has %zu bytes, %zu needed", stage_bytes, need);
+  if (!aligned16(stage)) return fail(VGGT3_EINVAL, "stage is not 16-byte aligned");
+  if (overlap(theta, theta_bytes(a), stage, stage_bytes)) return fail(VGGT3_EINVAL, "stage overlaps theta");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t hs = h2d_stream ? static_cast<hipStream_t>(h2d_stream) : s;
+  hipStream_t ds = d2h_stream ? static_cast<hipStream_t>(d2h_stream) : s;
+  CallEvents ev;
+  rc = check_hip(ev.create(7), "event create");
+  if (rc) return rc;
+  hipEvent_t entry = ev.e[0], q_in[2] = {ev.e[1], ev.e[2]}, done[2] = {ev.e[3], ev.e[4]},
+             o_out[2] = {ev.e[5], ev.e[6]};
+  rc = check_hip(hipEventRecord(entry, s), "event record");
+  if (!rc && hs != s) rc = check_hip(hipStreamWaitEvent(hs, entry, 0), "stream wait");
+  if (!rc && ds != s && ds != hs) rc = check_hip(hipStreamWaitEvent(ds, entry, 0), "stream wait");
+  if (rc) return rc;
+
+  const size_t row = (size_t)C * elem_size(dtype);
+  char* st = static_cast<char*>(stage);
+  const int64_t nc = (a.n + ct - 1) / ct;
+  auto chunk_len = [&](int64_t c) { return c + 1 < nc ? ct : a.n - c * ct; };
+  auto q_slot = [&](int64_t c) { return st + (size_t)(2 * (c & 1)) * slot; };
+  auto o_slot = [&](int64_t c) { return st + (size_t)(2 * (c & 1) + 1) * slot; };
+  // Copy chunk c's queries in once the read of chunk c-2 (same slot) is done.
+  auto fetch = [&](int64_t c) -> int {
+    int r = VGGT3_OK;
+    if (c >= 2 && hs != s) r = check_hip(hipStreamWaitEvent(hs, done[c & 1], 0), "stream wait");
+    if (!r)
+      r = check_hip(hipMemcpyAsync(q_slot(c), static_cast<const char*>(Q_host) + (size_t)(c * ct) * row,
+                                   (size_t)chunk_len(c) * row, hipMemcpyHostToDevice, hs),
+                    "Q copy");
+    if (!r && hs != s) r = check_hip(hipEventRecord(q_in[c & 1], hs), "event record");
+    return r;
+  };
+  rc = fetch(0);
+  if (rc) return rc;
+  for (int64_t c = 0; c < nc; ++c) {
+    if (c + 1 < nc) {
+      rc = fetch(c + 1);
+      if (rc) return rc;
+    }
+    const int sl = (int)(c & 1);
+    if (hs != s) rc = check_hip(hipStreamWaitEvent(s, q_in[sl], 0), "stream wait");
+    // The O slot is rewritten once chunk c-2's output has left it.
+    if (!rc && c >= 2 && ds != s) rc = check_hip(hipStreamWaitEvent(s, o_out[sl], 0), "stream wait");
+    if (rc) return rc;
+    const int64_t tn = chunk_len(c);
+    hipError_t e = dtype == VGGT3_BF16 ? vggt3::launch_read_bf16(q_slot(c), theta, o_slot(c), tn, n_heads, s)
+                                       : vggt3::launch_read_f32(q_slot(c), theta, o_slot(c), tn, n_heads, d_head,
+                                                                d_hidden, s);
+    rc = check_hip(e, "read kernel launch");
+    if (!rc) rc = check_hip(hipEventRecord(done[sl], s), "event record");
+    if (!rc && ds != s) rc = check_hip(hipStreamWaitEvent(ds, done[sl], 0), "stream wait");
+    if (!rc)
+      rc = check_hip(hipMemcpyAsync(static_cast<char*>(O_host) + (size_t)(c * ct) * row, o_slot(c),
+                                    (size_t)tn * row, hipMemcpyDeviceToHost, ds),
+                     "O copy");
+    if (!rc && ds != s) rc = check_hip(hipEventRecord(o_out[sl], ds), "event record");
+    if (rc) return rc;
+  }
+  // Later work on `stream` comes after the last copies out.
+  if (ds != s) {
+    rc = check_hip(hipStreamWaitEvent(s, o_out[(nc - 1) & 1], 0), "stream wait");
+    if (!rc && nc >= 2) rc = check_hip(hipStreamWaitEvent(s, o_out[(nc - 2) & 1], 0), "stream wait");
+    if (rc) return rc;
+  }
+  return ok();
 }
 
 }  // extern "C"

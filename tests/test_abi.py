@@ -183,3 +183,67 @@ def test_shortconv_ex_validation(lib):
     assert call(5, C=12) == tla.EUNSUPPORTED
     assert lib.vggt3_shortconv_ex(FAKE, FAKE, FAKE3, 2, 37, 37, 5, 1024, 5, tla.BF16, None) == tla.EINVAL
     assert lib.vggt3_shortconv_ex(FAKE, FAKE2, FAKE3, 0, 37, 37, 5, 1024, 5, tla.BF16, None) == tla.OK
+
+
+def test_streamed_entry_points_validate(lib):
+    n, H, d, m = 100_000, 16, 64, 128
+    ct = 8192
+    stage_need = lib.vggt3_ttt_stream_stage_bytes(ct, H, d, tla.BF16)
+    assert stage_need == 4 * ((ct * H * d * 2 + 255) // 256 * 256)
+    assert lib.vggt3_ttt_stream_stage_bytes(0, H, d, tla.BF16) == 0
+    assert lib.vggt3_ttt_stream_stage_bytes(ct, H, d, 9) == 0
+    assert lib.vggt3_ttt_stream_stage_bytes(1, 1, 16, tla.F32) == 4 * 256
+    ws_need = lib.vggt3_ttt_workspace_bytes(ct, H, d, m, tla.BF16)
+    stage = ctypes.c_void_p(0x7000000000)
+    ws = ctypes.c_void_p(0x7800000000)
+
+    def write(K=FAKE, Vp=FAKE2, theta=FAKE3, n=n, ct=ct, stage=stage, sb=stage_need, ws=ws, wsb=ws_need, steps=2,
+              loss=0, opt=0, ns=5, lr=0.1, loss_out=None, d=d, m=m):
+        return lib.vggt3_ttt_write_streamed(K, Vp, theta, n, H, d, m, lr, steps, loss, opt, ns, tla.BF16, ct, stage,
+                                            sb, ws, wsb, loss_out, None, None)
+
+    assert write(ct=0) == tla.EINVAL and "chunk_tokens" in _err(lib)
+    assert write(steps=0) == tla.EINVAL
+    assert write(lr=float("nan")) == tla.EINVAL
+    assert write(loss=5) == tla.EINVAL
+    assert write(opt=3) == tla.EINVAL
+    assert write(opt=1, ns=65) == tla.EINVAL
+    assert write(d=32) == tla.EUNSUPPORTED
+    assert write(K=None) == tla.EINVAL
+    assert write(theta=None) == tla.EINVAL
+    assert write(stage=None) == tla.EINVAL
+    assert write(sb=stage_need - 1) == tla.EWORKSPACE and "stage" in _err(lib)
+    assert write(ws=None) == tla.EWORKSPACE
+    assert write(wsb=ws_need - 1) == tla.EWORKSPACE
+    # the workspace is sized for one chunk, not for the scene
+    assert ws_need <= lib.vggt3_ttt_workspace_bytes(n, H, d, m, tla.BF16)
+    assert lib.vggt3_ttt_workspace_bytes(256, H, d, m, tla.BF16) < lib.vggt3_ttt_workspace_bytes(n, H, d, m, tla.BF16)
+    assert write(stage=ws) == tla.EINVAL and "overlap" in _err(lib)
+    assert write(theta=stage) == tla.EINVAL and "overlap" in _err(lib)
+    assert write(loss_out=stage) == tla.EINVAL and "overlap" in _err(lib)
+    # a chunk larger than the scene needs only the scene's staging
+    small = lib.vggt3_ttt_stream_stage_bytes(1000, H, d, tla.BF16)
+    assert write(n=1000, ct=10**9, sb=small - 1, wsb=10**9) == tla.EWORKSPACE
+    # empty scene without loss output: nothing enqueued
+    assert write(n=0, K=None, Vp=None, stage=None, ws=None) == tla.OK
+
+    def read(Q=FAKE, theta=FAKE3, O=FAKE2, n=n, ct=ct, stage=stage, sb=stage_need):
+        return lib.vggt3_ttt_read_streamed(Q, theta, O, n, H, d, m, tla.BF16, ct, stage, sb, None, None, None)
+
+    assert read(ct=-1) == tla.EINVAL
+    assert read(Q=None) == tla.EINVAL
+    assert read(O=FAKE) == tla.EINVAL and "overlap" in _err(lib)
+    assert read(stage=None) == tla.EINVAL
+    assert read(sb=stage_need - 16) == tla.EWORKSPACE
+    assert read(stage=FAKE3) == tla.EINVAL and "overlap" in _err(lib)
+    assert read(n=0, Q=None, O=None, stage=None) == tla.OK
+
+
+def test_streamed_binding_refuses_device_layout_mixups():
+    import torch
+    theta = torch.zeros(16, 3 * 64 * 128)
+    K = torch.zeros(64, 1024, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tla.ttt_write_streamed(K, K, theta, 0.1, 1, 16, 32)  # theta must be a device tensor
+    with pytest.raises(ValueError):
+        tla.ttt_read_streamed(K[:, ::2], theta, 16, 32, out=K[:, ::2])  # non-contiguous host tensor
