@@ -153,7 +153,12 @@ size_t vggt3_ttt_workspace_bytes(int64_t n_tokens, int32_t n_heads, int32_t d_he
  *             (may be NULL when that is 0).
  *   loss_out  NULL or float32 [steps][n_heads]: the loss at the theta each
  *             step starts from.
- * Supported (d_head, d_hidden): bf16 (64, 128); f32 (16, 32) and (64, 128).
+ * Supported (d_head, d_hidden): bf16 (64, 128); f32 (16, 32) and (64, 128);
+ * and bf16 (1024, 4096) with n_heads = 1, the pages' full-width MLP ([GRAPH]
+ * "TTT MLP Architecture and Inner Optimization": one 1024 -> 4096 -> 1024
+ * SwiGLU), written with gradient descent (either loss). Its workspace holds
+ * the intermediates of one chunk of up to 131,072 tokens (about 5.6 GB) plus
+ * split-K gradient partials; its read needs vggt3_ttt_read_ex.
  * n_tokens == 0 leaves theta unchanged (losses written as 0).
  */
 int vggt3_ttt_write(const void* K, const void* Vp, float* theta, int64_t n_tokens,
@@ -265,6 +270,24 @@ int vggt3_ttt_apply(float* theta, const float* grad, float lr, int32_t n_heads, 
  */
 int vggt3_ttt_read(const void* Q, const float* theta, void* O, int64_t n_tokens, int32_t n_heads,
                    int32_t d_head, int32_t d_hidden, int32_t dtype, void* stream);
+
+/*
+ * Bytes of device workspace vggt3_ttt_read_ex needs: 0 for the per-head
+ * shapes; for the full-width (1024, 4096) MLP, bf16 copies of the weights and
+ * the hidden activations of one token chunk.
+ */
+size_t vggt3_ttt_read_workspace_bytes(int64_t n_tokens, int32_t n_heads, int32_t d_head, int32_t d_hidden,
+                                      int32_t dtype);
+
+/*
+ * vggt3_ttt_read with a workspace (at least vggt3_ttt_read_workspace_bytes);
+ * the only read of the full-width (1024, 4096) MLP, which vggt3_ttt_read
+ * refuses with VGGT3_EUNSUPPORTED. For the per-head shapes the workspace is
+ * ignored. The workspace must not overlap Q, theta or O.
+ */
+int vggt3_ttt_read_ex(const void* Q, const float* theta, void* O, int64_t n_tokens, int32_t n_heads,
+                      int32_t d_head, int32_t d_hidden, int32_t dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /*
  * Streamed (offloaded) write and read: the scene's token tensors stay in HOST

@@ -213,15 +213,26 @@ def ttt_apply(theta: torch.Tensor, grad: torch.Tensor, lr: float, n_heads: int, 
     return theta
 
 
+def read_workspace_bytes(n_tokens: int, n_heads: int, d_head: int, d_hidden: int, dtype_code: int) -> int:
+    return int(lib().vggt3_ttt_read_workspace_bytes(n_tokens, n_heads, d_head, d_hidden, dtype_code))
+
+
 def ttt_read(Q: torch.Tensor, theta: torch.Tensor, n_heads: int, d_hidden: Optional[int] = None,
-             out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """O = T_theta(Q) per head."""
+             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """O = T_theta(Q) per head (the full-width 1024 -> 4096 MLP reads through a workspace)."""
     if out is None:
         out = torch.empty_like(Q)
-    _check_dev(Q, theta, out)
+    _check_dev(Q, theta, out, workspace)
     d, m = _mlp_dims(theta, Q, n_heads, d_hidden)
-    _call("vggt3_ttt_read", _ptr(Q), _ptr(theta), _ptr(out), Q.shape[0], n_heads, d, m, _dtype_code(Q),
-          _stream())
+    dt = _dtype_code(Q)
+    need = read_workspace_bytes(Q.shape[0], n_heads, d, m, dt)
+    if need == 0 and workspace is None:
+        _call("vggt3_ttt_read", _ptr(Q), _ptr(theta), _ptr(out), Q.shape[0], n_heads, d, m, dt, _stream())
+        return out
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    _call("vggt3_ttt_read_ex", _ptr(Q), _ptr(theta), _ptr(out), Q.shape[0], n_heads, d, m, dt, _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream())
     return out
 
 

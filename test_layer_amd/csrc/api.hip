@@ -8,6 +8,7 @@
 
 #include "../../include/vggt3.h"
 #include "kernels.hpp"
+#include "wide.hpp"
 
 namespace {
 
@@ -45,9 +46,12 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 bool valid_dtype(int32_t dt) { return dt == VGGT3_BF16 || dt == VGGT3_F32; }
 size_t elem_size(int32_t dt) { return dt == VGGT3_BF16 ? 2 : 4; }
 
+// The pages' full-width MLP: one 1024 -> 4096 -> 1024 SwiGLU (one "head").
+bool is_wide(int32_t d, int32_t m) { return d == vggt3::wide::kD && m == vggt3::wide::kM; }
+
 // Shapes with a kernel in this build.
 bool supported_mlp(int32_t dt, int32_t d, int32_t m) {
-  if (dt == VGGT3_BF16) return d == 64 && m == 128;
+  if (dt == VGGT3_BF16) return (d == 64 && m == 128) || is_wide(d, m);
   if (dt == VGGT3_F32) return (d == 16 && m == 32) || (d == 64 && m == 128);
   return false;
 }
@@ -68,6 +72,8 @@ int check_mlp(const MlpArgs& a) {
     return fail(VGGT3_EUNSUPPORTED, "no %s kernel for d_head = %d, d_hidden = %d",
                 a.dt == VGGT3_BF16 ? "bf16" : "f32", a.d, a.m);
   if ((int64_t)a.H * a.d > (int64_t)1 << 20) return fail(VGGT3_EUNSUPPORTED, "too many channels");
+  if (is_wide(a.d, a.m) && a.H != 1)
+    return fail(VGGT3_EUNSUPPORTED, "the %d -> %d -> %d MLP takes n_heads = 1 (got %d)", a.d, a.m, a.d, a.H);
   return VGGT3_OK;
 }
 
@@ -90,11 +96,169 @@ WsLayout ws_layout(const MlpArgs& a, int P) {
   return l;
 }
 
+// Workspace of the wide MLP (write and read), for tokens processed in chunks
+// of at most wide::kChunk: bf16 GEMM operands of theta, the chunk's
+// intermediates, the split-K gradient partials, one reduced gradient and the
+// loss partials.
+struct WideWs {
+  int64_t ct, ctp, nchunks, loss_stride;
+  size_t wgu, wdt, wdn, h, a, gp, dgu, y, pgu, pd, grad, loss, total, read_total;
+};
+WideWs wide_ws(int64_t n) {
+  namespace w = vggt3::wide;
+  WideWs l{};
+  l.ct = n < w::kChunk ? n : w::kChunk;
+  if (l.ct < 1) l.ct = 1;
+  l.ctp = (l.ct + w::kTile - 1) / w::kTile * w::kTile;
+  l.nchunks = (n + l.ct - 1) / l.ct;
+  l.loss_stride = (l.ctp / w::kTile) * (w::kM / w::kTile);
+  const size_t d = w::kD, m = w::kM, ctp = (size_t)l.ctp;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round256(bytes);
+    return at;
+  };
+  l.wgu = take(2 * m * d * 2);
+  l.wdt = take(d * m * 2);
+  l.wdn = take(m * d * 2);
+  l.h = take(ctp * m * 2);
+  l.read_total = o;
+  l.a = take(ctp * m * 2);
+  l.gp = take(ctp * m * 2);
+  l.dgu = take(ctp * 2 * m * 2);
+  l.y = take(ctp * d * 2);
+  l.pgu = take((size_t)w::kSplit * d * 2 * m * 4);
+  l.pd = take((size_t)w::kSplit * m * d * 4);
+  l.grad = take(3 * d * m * 4);
+  l.loss = take((size_t)l.nchunks * l.loss_stride * 4);
+  l.total = o;
+  return l;
+}
+
 size_t workspace_bytes(const MlpArgs& a, int* P_out) {
+  if (is_wide(a.d, a.m)) {
+    if (P_out) *P_out = 1;
+    return a.n == 0 ? 0 : wide_ws(a.n).total;
+  }
   const int P = vggt3::ttt_num_chunks(a.n, a.H, tile_tokens(a.dt));
   if (P_out) *P_out = P;
   if (a.n == 0) return 0;
   return ws_layout(a, P).total;
+}
+
+// One gradient pass of the wide MLP over all n tokens at theta: the gradient
+// (times `scale` inside the reduce) goes to dst in `mode` (apply with lr,
+// store, accumulate); the loss to loss_out (stored, or added if loss_acc).
+int wide_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& a, int32_t loss, void* ws,
+              vggt3::ReduceMode mode, float* dst, float lr, float* loss_out, int loss_acc, hipStream_t s) {
+  namespace w = vggt3::wide;
+  const WideWs l = wide_ws(a.n);
+  char* base = static_cast<char*>(ws);
+  auto bf = [&](size_t off) { return reinterpret_cast<uint16_t*>(base + off); };
+  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+  const int d = w::kD, m = w::kM;
+  const bool dot = loss == VGGT3_LOSS_DOT;
+  int rc = check_hip(w::launch_pack(theta, bf(l.wgu), bf(l.wdt), bf(l.wdn), d, m, s), "pack launch");
+  if (!rc && loss_out)
+    rc = check_hip(vggt3::launch_fill(f32(l.loss), 0.0f, l.nchunks * l.loss_stride, s), "fill launch");
+  if (rc) return rc;
+  const uint16_t* Kb = static_cast<const uint16_t*>(K);
+  const uint16_t* Vb = static_cast<const uint16_t*>(Vp);
+  for (int64_t c = 0; c < l.nchunks; ++c) {
+    const int64_t t0 = c * l.ct, nc = a.n - t0 < l.ct ? a.n - t0 : l.ct;
+    const uint16_t* Kc = Kb + t0 * d;
+    const uint16_t* Vc = Vb + t0 * d;
+    float* lossc = f32(l.loss) + c * l.loss_stride;
+    w::GemmArgs g{};
+    // P1: [G | U] = K [W_g | W_u] -> H, A, GP
+    g.M = nc; g.N = 2 * m; g.K = d; g.nseg = 1; g.S = 1;
+    g.A[0] = Kc; g.lda[0] = d; g.B[0] = bf(l.wgu); g.ldb[0] = d;
+    g.out0 = bf(l.h); g.out1 = bf(l.a); g.out2 = bf(l.gp); g.ldo = m;
+    rc = check_hip(w::launch_gemm(w::EPI_SWIGLU, g, s), "wide gemm P1");
+    if (rc) return rc;
+    if (!dot) {
+      // P2: Y = H W_d -> -Y, loss partials
+      g = w::GemmArgs{};
+      g.M = nc; g.N = d; g.K = m; g.nseg = 1; g.S = 1;
+      g.A[0] = bf(l.h); g.lda[0] = m; g.B[0] = bf(l.wdt); g.ldb[0] = m;
+      g.out0 = bf(l.y); g.ldo = d; g.in0 = Vc; g.ldi = d; g.fout = lossc;
+      rc = check_hip(w::launch_gemm(w::EPI_Y_LOSS, g, s), "wide gemm P2");
+      if (rc) return rc;
+    }
+    // P3: D = [-Y | V'] [W_d ; W_d]^T (dot: D = V' W_d^T) -> [dG | dU]
+    g = w::GemmArgs{};
+    g.M = nc; g.N = m; g.K = d; g.S = 1;
+    if (dot) {
+      g.nseg = 1; g.A[0] = Vc; g.lda[0] = d; g.B[0] = bf(l.wdn); g.ldb[0] = d;
+      g.in2 = bf(l.h); g.fout = lossc;
+    } else {
+      g.nseg = 2;
+      g.A[0] = bf(l.y); g.lda[0] = d; g.A[1] = Vc; g.lda[1] = d;
+      g.B[0] = bf(l.wdn); g.ldb[0] = d; g.B[1] = bf(l.wdn); g.ldb[1] = d;
+    }
+    g.in0 = bf(l.gp); g.in1 = bf(l.a); g.out0 = bf(l.dgu); g.ldo = 2 * m;
+    rc = check_hip(w::launch_gemm(dot ? w::EPI_DH_DOT : w::EPI_DH, g, s), "wide gemm P3");
+    if (rc) return rc;
+    // P4: [gW_g | gW_u] += K^T [dG | dU];  gW_d += H^T (-Y) + H^T V' (dot: H^T V')
+    g = w::GemmArgs{};
+    g.M = d; g.N = 2 * m; g.K = nc; g.nseg = 1; g.S = w::kSplit;
+    g.A[0] = Kc; g.lda[0] = d; g.B[0] = bf(l.dgu); g.ldb[0] = 2 * m;
+    g.a_rows[0] = nc; g.b_rows[0] = l.ctp;  // [dG | dU] rows nc .. ctp are zeros
+    g.fout = f32(l.pgu); g.accumulate = c > 0;
+    rc = check_hip(w::launch_gemm(w::EPI_PARTIAL, g, s), "wide gemm P4a");
+    if (rc) return rc;
+    g = w::GemmArgs{};
+    g.M = m; g.N = d; g.K = nc; g.S = w::kSplit;
+    // H rows nc .. ctp are zeros
+    if (dot) {
+      g.nseg = 1; g.A[0] = bf(l.h); g.lda[0] = m; g.B[0] = Vc; g.ldb[0] = d;
+      g.a_rows[0] = l.ctp; g.b_rows[0] = nc;
+    } else {
+      g.nseg = 2;
+      g.A[0] = bf(l.h); g.lda[0] = m; g.A[1] = bf(l.h); g.lda[1] = m;
+      g.B[0] = bf(l.y); g.ldb[0] = d; g.B[1] = Vc; g.ldb[1] = d;
+      g.a_rows[0] = g.a_rows[1] = l.ctp; g.b_rows[0] = g.b_rows[1] = nc;
+    }
+    g.fout = f32(l.pd); g.accumulate = c > 0;
+    rc = check_hip(w::launch_gemm(w::EPI_PARTIAL, g, s), "wide gemm P4b");
+    if (rc) return rc;
+  }
+  const float gscale = dot ? -1.0f : -2.0f / d;
+  rc = check_hip(w::launch_reduce_partials(f32(l.pgu), f32(l.pd), w::kSplit, d, m, gscale, (int)mode, dst, lr, s),
+                 "wide reduce launch");
+  if (!rc && loss_out)
+    rc = check_hip(w::launch_sum(f32(l.loss), l.nchunks * l.loss_stride, dot ? -1.0f : 1.0f / d, loss_acc, loss_out,
+                                 s),
+                   "loss sum launch");
+  return rc;
+}
+
+// Read of the wide MLP: per chunk, H = SwiGLU(Q) then O = H W_d.
+int wide_read(const void* Q, const float* theta, void* O, const MlpArgs& a, void* ws, hipStream_t s) {
+  namespace w = vggt3::wide;
+  const WideWs l = wide_ws(a.n);
+  char* base = static_cast<char*>(ws);
+  auto bf = [&](size_t off) { return reinterpret_cast<uint16_t*>(base + off); };
+  const int d = w::kD, m = w::kM;
+  int rc = check_hip(w::launch_pack(theta, bf(l.wgu), bf(l.wdt), bf(l.wdn), d, m, s), "pack launch");
+  if (rc) return rc;
+  for (int64_t c = 0; c < l.nchunks; ++c) {
+    const int64_t t0 = c * l.ct, nc = a.n - t0 < l.ct ? a.n - t0 : l.ct;
+    w::GemmArgs g{};
+    g.M = nc; g.N = 2 * m; g.K = d; g.nseg = 1; g.S = 1;
+    g.A[0] = static_cast<const uint16_t*>(Q) + t0 * d; g.lda[0] = d; g.B[0] = bf(l.wgu); g.ldb[0] = d;
+    g.out0 = bf(l.h); g.ldo = m;
+    rc = check_hip(w::launch_gemm(w::EPI_SWIGLU_H, g, s), "wide gemm R1");
+    if (rc) return rc;
+    g = w::GemmArgs{};
+    g.M = nc; g.N = d; g.K = m; g.nseg = 1; g.S = 1;
+    g.A[0] = bf(l.h); g.lda[0] = m; g.B[0] = bf(l.wdt); g.ldb[0] = m;
+    g.out0 = static_cast<uint16_t*>(O) + t0 * d; g.ldo = d;
+    rc = check_hip(w::launch_gemm(w::EPI_Y_STORE, g, s), "wide gemm R2");
+    if (rc) return rc;
+  }
+  return VGGT3_OK;
 }
 
 bool valid_loss(int32_t loss) { return loss == VGGT3_LOSS_MSE || loss == VGGT3_LOSS_DOT; }
@@ -243,10 +407,22 @@ int vggt3_ttt_write_ex(const void* K, const void* Vp, float* theta, int64_t n_to
   if (overlap(loss_out, lb, workspace, workspace_bytes_) || overlap(loss_out, lb, K, xb) ||
       overlap(loss_out, lb, Vp, xb))
     return fail(VGGT3_EINVAL, "loss_out overlaps another argument");
+  if (overlap(workspace, workspace_bytes_, K, xb) || overlap(workspace, workspace_bytes_, Vp, xb))
+    return fail(VGGT3_EINVAL, "workspace overlaps K or V'");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.n == 0) {
     if (loss_out) {
       rc = check_hip(vggt3::launch_fill(loss_out, 0.0f, (int64_t)steps * n_heads, s), "fill launch");
+      if (rc) return rc;
+    }
+    return ok();
+  }
+  if (is_wide(a.d, a.m)) {
+    if (optimizer != VGGT3_OPT_GD)
+      return fail(VGGT3_EUNSUPPORTED, "the %d -> %d -> %d MLP is written with gradient descent only", a.d, a.m, a.d);
+    for (int st = 0; st < steps; ++st) {
+      rc = wide_grad(K, Vp, theta, a, loss, workspace, vggt3::kApply, theta, lr,
+                     loss_out ? loss_out + (size_t)st * n_heads : nullptr, 0, s);
       if (rc) return rc;
     }
     return ok();
@@ -297,6 +473,9 @@ int vggt3_ttt_grad_ex(const void* K, const void* Vp, const float* theta, float* 
     return fail(VGGT3_EINVAL, "grad overlaps another argument");
   if (overlap(loss_out, lb, workspace, workspace_bytes_) || overlap(loss_out, lb, theta, tb))
     return fail(VGGT3_EINVAL, "loss_out overlaps another argument");
+  if (overlap(workspace, workspace_bytes_, theta, tb) || overlap(workspace, workspace_bytes_, K, xb) ||
+      overlap(workspace, workspace_bytes_, Vp, xb))
+    return fail(VGGT3_EINVAL, "workspace overlaps theta, K or V'");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.n == 0) {
     if (!accumulate) {
@@ -306,8 +485,12 @@ int vggt3_ttt_grad_ex(const void* K, const void* Vp, const float* theta, float* 
     }
     return ok();
   }
-  rc = run_grad(K, Vp, theta, a, workspace, P, loss, accumulate ? vggt3::kAccum : vggt3::kStore, grad, 0.0f,
-                loss_out, s);
+  if (is_wide(a.d, a.m))
+    rc = wide_grad(K, Vp, theta, a, loss, workspace, accumulate ? vggt3::kAccum : vggt3::kStore, grad, 0.0f,
+                   loss_out, accumulate ? 1 : 0, s);
+  else
+    rc = run_grad(K, Vp, theta, a, workspace, P, loss, accumulate ? vggt3::kAccum : vggt3::kStore, grad, 0.0f,
+                  loss_out, s);
   return rc ? rc : ok();
 }
 
@@ -325,6 +508,7 @@ int vggt3_ttt_grad_partials_ex(const void* K, const void* Vp, const float* theta
   int rc = check_mlp(a);
   if (rc) return rc;
   if (!valid_loss(loss)) return fail(VGGT3_EINVAL, "unknown loss %d", loss);
+  if (is_wide(a.d, a.m)) return fail(VGGT3_EUNSUPPORTED, "no per-chunk partials for the %d -> %d MLP", a.d, a.m);
   if (theta == nullptr) return fail(VGGT3_EINVAL, "theta is NULL");
   if (!aligned16(theta)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
   if (a.n == 0) return ok();
@@ -357,6 +541,7 @@ int vggt3_ttt_reduce(const void* workspace, size_t workspace_bytes_, int64_t n_t
   if (rc) return rc;
   if (mode != VGGT3_REDUCE_APPLY && mode != VGGT3_REDUCE_STORE && mode != VGGT3_REDUCE_ACCUMULATE)
     return fail(VGGT3_EINVAL, "unknown reduce mode %d", mode);
+  if (is_wide(a.d, a.m)) return fail(VGGT3_EUNSUPPORTED, "no per-chunk partials for the %d -> %d MLP", a.d, a.m);
   if (!std::isfinite(lr)) return fail(VGGT3_EINVAL, "lr is not finite");
   if (dst == nullptr) return fail(VGGT3_EINVAL, "dst is NULL");
   if (!aligned16(dst) || (loss_out && !aligned16(loss_out))) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
@@ -425,6 +610,8 @@ int vggt3_ttt_read(const void* Q, const float* theta, void* O, int64_t n_tokens,
   const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
   int rc = check_mlp(a);
   if (rc) return rc;
+  if (is_wide(a.d, a.m))
+    return fail(VGGT3_EUNSUPPORTED, "the %d -> %d MLP needs a workspace: use vggt3_ttt_read_ex", a.d, a.m);
   if (a.n == 0) return ok();
   if (Q == nullptr || theta == nullptr || O == nullptr) return fail(VGGT3_EINVAL, "NULL pointer");
   if (!aligned16(Q) || !aligned16(theta) || !aligned16(O)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
@@ -434,6 +621,36 @@ int vggt3_ttt_read(const void* Q, const float* theta, void* O, int64_t n_tokens,
   hipError_t e = dtype == VGGT3_BF16 ? vggt3::launch_read_bf16(Q, theta, O, a.n, a.H, s)
                                      : vggt3::launch_read_f32(Q, theta, O, a.n, a.H, a.d, a.m, s);
   rc = check_hip(e, "read kernel launch");
+  return rc ? rc : ok();
+}
+
+size_t vggt3_ttt_read_workspace_bytes(int64_t n_tokens, int32_t n_heads, int32_t d_head, int32_t d_hidden,
+                                      int32_t dtype) {
+  const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
+  if (check_mlp(a) != VGGT3_OK || a.n == 0 || !is_wide(a.d, a.m)) return 0;
+  return wide_ws(a.n).read_total;
+}
+
+int vggt3_ttt_read_ex(const void* Q, const float* theta, void* O, int64_t n_tokens, int32_t n_heads, int32_t d_head,
+                      int32_t d_hidden, int32_t dtype, void* workspace, size_t workspace_bytes_, void* stream) {
+  const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
+  int rc = check_mlp(a);
+  if (rc) return rc;
+  if (!is_wide(a.d, a.m))
+    return vggt3_ttt_read(Q, theta, O, n_tokens, n_heads, d_head, d_hidden, dtype, stream);
+  if (a.n == 0) return ok();
+  if (Q == nullptr || theta == nullptr || O == nullptr) return fail(VGGT3_EINVAL, "NULL pointer");
+  if (!aligned16(Q) || !aligned16(theta) || !aligned16(O)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  const size_t need = wide_ws(a.n).read_total;
+  if (workspace == nullptr) return fail(VGGT3_EWORKSPACE, "workspace is NULL, %zu bytes needed", need);
+  if (workspace_bytes_ < need) return fail(VGGT3_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_, need);
+  if (!aligned16(workspace)) return fail(VGGT3_EINVAL, "workspace is not 16-byte aligned");
+  const size_t tb = theta_bytes(a), xb = token_bytes(a);
+  if (overlap(O, xb, Q, xb) || overlap(O, xb, theta, tb) || overlap(O, xb, workspace, workspace_bytes_))
+    return fail(VGGT3_EINVAL, "O overlaps Q, theta or the workspace");
+  if (overlap(workspace, workspace_bytes_, Q, xb) || overlap(workspace, workspace_bytes_, theta, tb))
+    return fail(VGGT3_EINVAL, "workspace overlaps Q or theta");
+  rc = wide_read(Q, theta, O, a, workspace, static_cast<hipStream_t>(stream));
   return rc ? rc : ok();
 }
 
@@ -461,6 +678,7 @@ int vggt3_ttt_write_streamed(const void* K_host, const void* Vp_host, float* the
   if (!std::isfinite(lr)) return fail(VGGT3_EINVAL, "lr is not finite");
   if (steps < 1) return fail(VGGT3_EINVAL, "steps = %d < 1", steps);
   if (chunk_tokens < 1) return fail(VGGT3_EINVAL, "chunk_tokens = %lld < 1", (long long)chunk_tokens);
+  if (is_wide(a.d, a.m)) return fail(VGGT3_EUNSUPPORTED, "no streamed write for the %d -> %d MLP", a.d, a.m);
   if (theta == nullptr) return fail(VGGT3_EINVAL, "theta is NULL");
   if (!aligned16(theta) || (loss_out && !aligned16(loss_out)))
     return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
@@ -565,6 +783,7 @@ int vggt3_ttt_read_streamed(const void* Q_host, const float* theta, void* O_host
   int rc = check_mlp(a);
   if (rc) return rc;
   if (chunk_tokens < 1) return fail(VGGT3_EINVAL, "chunk_tokens = %lld < 1", (long long)chunk_tokens);
+  if (is_wide(a.d, a.m)) return fail(VGGT3_EUNSUPPORTED, "no streamed read for the %d -> %d MLP", a.d, a.m);
   if (a.n == 0) return ok();
   if (Q_host == nullptr || theta == nullptr || O_host == nullptr) return fail(VGGT3_EINVAL, "NULL pointer");
   if (!aligned16(theta)) return fail(VGGT3_EINVAL, "theta is not 16-byte aligned");

@@ -1,0 +1,120 @@
+"""Parity of the full-width fast-weight MLP on the GPU: one 1024 -> 4096 -> 1024
+SwiGLU over the whole token ([GRAPH] "TTT MLP Architecture and Inner
+Optimization"), written with gradient descent under the squared-error or the
+dot-product loss, then read.
+
+The oracle is the same per-head oracle with one head of d = 1024, m = 4096
+(its pins are shape-generic). Bars: 2e-2 normwise per weight matrix and on the
+read (bf16 compute), Eq. 5 chunk splits to fp32 rounding (1e-5).
+"""
+from __future__ import annotations
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import test_layer_amd as tla
+from synth import CONFIGS, make_inputs
+from tests.gpu_util import bits, dtheta_ok, rel_err, rel_err_per_head, to64
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+DEV = "cuda"
+D, M = 1024, 4096
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tla.lib()
+
+
+def _cfg(views=1, grid=37, special=5, steps=1):
+    return replace(CONFIGS["views24"], name=f"wide{views}v", n_views=views, grid_h=grid, grid_w=grid,
+                   n_special=special, n_heads=1, d_head=D, d_hidden=M, steps=steps)
+
+
+def _scene(cfg, with_q=False):
+    inp = make_inputs(cfg, DEV, with_q=with_q)
+    Vp = tla.shortconv(inp.V, inp.conv_w, cfg.n_views, cfg.grid_h, cfg.grid_w, cfg.n_special)
+    torch.cuda.synchronize()
+    return inp, Vp
+
+
+def _oracle_vp(inp):
+    c = inp.cfg
+    return oracle.shortconv(to64(inp.V).astype(np.float32), inp.conv_w.cpu().numpy(), c.n_views, c.grid_h,
+                            c.grid_w, c.n_special, out="bf16").astype(np.float64)
+
+
+def _per_matrix_err(g, ref):
+    out = []
+    for a, b in zip(oracle.split_theta(g.reshape(-1), D, M), oracle.split_theta(ref.reshape(-1), D, M)):
+        out.append(rel_err(a, b))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("loss", ["mse", "dot"])
+def test_wide_gradient_parity(loss):
+    # one view of 37x37 + 5 tokens: 1,374 tokens = 5 full 256-token tiles + a ragged one
+    cfg = _cfg()
+    print(f"[wide] gradient {loss}", flush=True)
+    inp, Vp = _scene(cfg)
+    L = torch.empty(1, device=DEV)
+    g = tla.ttt_grad(inp.K, Vp, inp.theta0, 1, loss_out=L, loss=loss)
+    torch.cuda.synchronize()
+    th0 = inp.theta0.cpu().numpy()
+    g_ref, L_ref = oracle.ttt_grad(to64(inp.K), _oracle_vp(inp), th0, 1, D, M, loss=loss)
+    e = _per_matrix_err(to64(g), g_ref)
+    le = abs(L.item() - L_ref[0]) / abs(L_ref[0])
+    print(f"  per-matrix rel err {e}, loss {le:.3e}", flush=True)
+    assert e.max() <= TOL, e
+    if loss == "mse":
+        assert le <= TOL, le
+
+
+def test_wide_write_two_steps_parity():
+    cfg = _cfg(steps=2)
+    inp, Vp = _scene(cfg)
+    theta = inp.theta0.clone()
+    L = torch.empty((2, 1), device=DEV)
+    tla.ttt_write(inp.K, Vp, theta, cfg.lr, 2, 1, loss_out=L)
+    torch.cuda.synchronize()
+    th0 = inp.theta0.cpu().numpy()
+    th_ref, L_ref, _ = oracle.ttt_write(to64(inp.K), _oracle_vp(inp), th0, 1, D, M, cfg.lr, 2)
+    ok, worst = dtheta_ok(theta.cpu().numpy().astype(np.float64), th_ref, th0, 1, TOL, 2)
+    print(f"  wide write dtheta worst/allowance {worst:.3f}", flush=True)
+    assert ok, worst
+    np.testing.assert_allclose(L.cpu().numpy(), L_ref, rtol=TOL)
+
+
+def test_wide_read_parity():
+    cfg = _cfg()
+    inp = make_inputs(cfg, DEV, with_q=True)
+    theta = inp.theta0 * 10.0
+    O = tla.ttt_read(inp.Q, theta, 1)
+    torch.cuda.synchronize()
+    O_ref = oracle.ttt_read(to64(inp.Q), theta.cpu().numpy(), 1, D, M)
+    e = rel_err(to64(O), O_ref)
+    print(f"  wide read rel err {e:.3e}", flush=True)
+    assert e <= TOL, e
+
+
+def test_wide_gradient_eq5_split_and_determinism():
+    cfg = _cfg(views=2)
+    inp, Vp = _scene(cfg)
+    n = cfg.n_tokens
+    g = tla.ttt_grad(inp.K, Vp, inp.theta0, 1)
+    g2 = tla.ttt_grad(inp.K, Vp, inp.theta0, 1)
+    cut = 1000
+    acc = tla.ttt_grad(inp.K[:cut], Vp[:cut], inp.theta0, 1)
+    tla.ttt_grad(inp.K[cut:n], Vp[cut:n], inp.theta0, 1, grad=acc, accumulate=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(g), bits(g2))
+    e = _per_matrix_err(to64(acc), to64(g))
+    assert e.max() <= 1e-5, e
