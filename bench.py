@@ -39,6 +39,7 @@ RECIPES = {
     # name: (loss, optimizer, description)
     "mse_gd": ("mse", "gd", "mean-squared inner loss, plain gradient descent"),
     "dot_muon": ("dot", "muon", "the pages' recipe: dot-product inner loss, Muon update (5 Newton-Schulz steps)"),
+    "dot_gd": ("dot", "gd", "dot-product inner loss, plain gradient descent"),
 }
 
 
@@ -183,6 +184,111 @@ def offload_bench(tla, inp, Vp, cfg, args, loss_kind, opt_kind):
     }
 
 
+def wide_bench(args, loss_kind, opt_kind, recipe_desc):
+    """The pages' full-width fast-weight MLP (one 1024 -> 4096 -> 1024 SwiGLU
+    over the whole token) on the same scene: conv, `steps` write steps through
+    vggt3_ttt_write_ex (a chunked sequence of bf16 MFMA GEMMs with fused
+    epilogues), read through vggt3_ttt_read_ex. The roofline is that of the
+    write's GEMM sequence as a whole: algorithmic flops over its event time."""
+    import dataclasses
+
+    import torch
+
+    import test_layer_amd as tla
+    from synth import CONFIGS, make_inputs
+
+    base = CONFIGS[args.config]
+    cfg = dataclasses.replace(
+        base, name=f"{base.name}_wide", n_heads=1, d_head=1024, d_hidden=4096,
+        description=(f"{base.n_views} views = {base.n_tokens:,} tokens, one 1024 -> 4096 -> 1024 SwiGLU fast-weight "
+                     f"MLP, {base.steps} steps + full read"))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(cfg, dev)
+    n, d, m = cfg.n_tokens, cfg.d_head, cfg.d_hidden
+    Vp = torch.empty_like(inp.V)
+    O = torch.empty_like(inp.Q)
+    theta = inp.theta0.clone()
+    ws = tla.make_workspace(n, 1, d, m, tla.BF16, dev)
+    rws = torch.empty(tla.read_workspace_bytes(n, 1, d, m, tla.BF16), dtype=torch.uint8, device=dev)
+    loss = torch.zeros((cfg.steps, 1), device=dev)
+
+    def step(ev=None):
+        theta.copy_(inp.theta0)
+        if ev:
+            ev[0].record()
+        tla.shortconv(inp.V, inp.conv_w, cfg.n_views, cfg.grid_h, cfg.grid_w, cfg.n_special, out=Vp)
+        if ev:
+            ev[1].record()
+        tla.ttt_write(inp.K, Vp, theta, cfg.lr, cfg.steps, 1, workspace=ws, loss_out=loss, loss=loss_kind,
+                      optimizer=opt_kind)
+        if ev:
+            ev[2].record()
+        tla.ttt_read(inp.Q, theta, 1, out=O, workspace=rws)
+        if ev:
+            ev[3].record()
+
+    def mk():
+        return torch.cuda.Event(enable_timing=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[mk() for _ in range(4)] for _ in range(args.steps)]
+    start, end = mk(), mk()
+    start.record()
+    for i in range(args.steps):
+        step(events[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    conv_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    write_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    read_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    fw, fr = flops_per_token(cfg, loss_kind)
+    achieved = fw * n * cfg.steps / (write_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": n / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.description}",
+            "n_views": cfg.n_views, "tokens_per_view": cfg.tokens_per_view, "n_tokens": n,
+            "n_heads": 1, "d_head": d, "d_hidden": m, "write_steps": cfg.steps, "lr": cfg.lr,
+            "read_tokens": inp.Q.shape[0], "parallelism": "single GPU", "recipe": f"{args.recipe}: {recipe_desc}",
+            "conv_variant": "3x3 on V",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "wide write: per token chunk P1-P4 bf16 GEMMs (gemm_kernel<...>) + reduce",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "avg_launch_ms": write_ms / cfg.steps,
+            "flops_per_launch": fw * n,
+        },
+        "phases_ms": {"conv": conv_ms, "write": write_ms, "read": read_ms},
+        "mfma_frac_mlp_contractions": (fw * n * cfg.steps + fr * inp.Q.shape[0]) / ((write_ms + read_ms) * 1e-3)
+                                      / 1e12 / PEAK_BF16_TFLOPS,
+        "read_TFLOPs": fr * inp.Q.shape[0] / (read_ms * 1e-3) / 1e12,
+        "final_loss": float(loss[-1, 0].item()),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, cfg, loss=loss_kind, opt=opt_kind)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +299,9 @@ def main():
                     help="inner loss and update rule (default: squared error + gradient descent)")
     ap.add_argument("--conv-variant", default="v3", choices=["v3", "v5", "kv3"],
                     help="ShortConv2D variant of the pages' Table 9: 3x3 on V (default), 5x5 on V, 3x3 on K and V")
+    ap.add_argument("--mlp", default="per-head", choices=["per-head", "wide"],
+                    help="fast-weight MLP: 16 per-head SwiGLUs 64 -> 128 -> 64 (default) or the pages' full-width "
+                         "1024 -> 4096 -> 1024 SwiGLU")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--offload", type=int, default=0, metavar="CHUNK",
                     help="also time the offloaded step (K, V', Q in pinned host memory, streamed through the GPU in "
@@ -214,6 +323,13 @@ def main():
 
     cfg = CONFIGS[args.config]
     loss_kind, opt_kind, recipe_desc = RECIPES[args.recipe]
+    if args.mlp == "wide":
+        if opt_kind != "gd":
+            print("bench.py: the full-width MLP is written with gradient descent (--recipe mse_gd or dot_gd)",
+                  file=sys.stderr)
+            sys.exit(2)
+        wide_bench(args, loss_kind, opt_kind, recipe_desc)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = make_inputs(cfg, dev)

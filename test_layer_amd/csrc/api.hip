@@ -98,8 +98,8 @@ WsLayout ws_layout(const MlpArgs& a, int P) {
 
 // Workspace of the wide MLP (write and read), for tokens processed in chunks
 // of at most wide::kChunk: bf16 GEMM operands of theta, the chunk's
-// intermediates, the split-K gradient partials, one reduced gradient and the
-// loss partials.
+// intermediates, the split-K gradient partials, one reduced gradient and one
+// chunk's loss partials.
 struct WideWs {
   int64_t ct, ctp, nchunks, loss_stride;
   size_t wgu, wdt, wdn, h, a, gp, dgu, y, pgu, pd, grad, loss, total, read_total;
@@ -131,7 +131,7 @@ WideWs wide_ws(int64_t n) {
   l.pgu = take((size_t)w::kSplit * d * 2 * m * 4);
   l.pd = take((size_t)w::kSplit * m * d * 4);
   l.grad = take(3 * d * m * 4);
-  l.loss = take((size_t)l.nchunks * l.loss_stride * 4);
+  l.loss = take((size_t)l.loss_stride * 4);
   l.total = o;
   return l;
 }
@@ -160,16 +160,15 @@ int wide_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& 
   const int d = w::kD, m = w::kM;
   const bool dot = loss == VGGT3_LOSS_DOT;
   int rc = check_hip(w::launch_pack(theta, bf(l.wgu), bf(l.wdt), bf(l.wdn), d, m, s), "pack launch");
-  if (!rc && loss_out)
-    rc = check_hip(vggt3::launch_fill(f32(l.loss), 0.0f, l.nchunks * l.loss_stride, s), "fill launch");
   if (rc) return rc;
+  const float lscale = dot ? -1.0f : 1.0f / d;
   const uint16_t* Kb = static_cast<const uint16_t*>(K);
   const uint16_t* Vb = static_cast<const uint16_t*>(Vp);
   for (int64_t c = 0; c < l.nchunks; ++c) {
     const int64_t t0 = c * l.ct, nc = a.n - t0 < l.ct ? a.n - t0 : l.ct;
     const uint16_t* Kc = Kb + t0 * d;
     const uint16_t* Vc = Vb + t0 * d;
-    float* lossc = f32(l.loss) + c * l.loss_stride;
+    float* lossc = f32(l.loss);
     w::GemmArgs g{};
     // P1: [G | U] = K [W_g | W_u] -> H, A, GP
     g.M = nc; g.N = 2 * m; g.K = d; g.nseg = 1; g.S = 1;
@@ -200,6 +199,12 @@ int wide_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& 
     g.in0 = bf(l.gp); g.in1 = bf(l.a); g.out0 = bf(l.dgu); g.ldo = 2 * m;
     rc = check_hip(w::launch_gemm(dot ? w::EPI_DH_DOT : w::EPI_DH, g, s), "wide gemm P3");
     if (rc) return rc;
+    if (loss_out) {
+      // this chunk's per-workgroup loss sums (P2, or P3 for the dot loss)
+      const int64_t nt = (nc + w::kTile - 1) / w::kTile * ((dot ? m : d) / w::kTile);
+      rc = check_hip(w::launch_sum(lossc, nt, lscale, c > 0 ? 1 : loss_acc, loss_out, s), "loss sum launch");
+      if (rc) return rc;
+    }
     // P4: [gW_g | gW_u] += K^T [dG | dU];  gW_d += H^T (-Y) + H^T V' (dot: H^T V')
     g = w::GemmArgs{};
     g.M = d; g.N = 2 * m; g.K = nc; g.nseg = 1; g.S = w::kSplit;
@@ -227,10 +232,6 @@ int wide_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& 
   const float gscale = dot ? -1.0f : -2.0f / d;
   rc = check_hip(w::launch_reduce_partials(f32(l.pgu), f32(l.pd), w::kSplit, d, m, gscale, (int)mode, dst, lr, s),
                  "wide reduce launch");
-  if (!rc && loss_out)
-    rc = check_hip(w::launch_sum(f32(l.loss), l.nchunks * l.loss_stride, dot ? -1.0f : 1.0f / d, loss_acc, loss_out,
-                                 s),
-                   "loss sum launch");
   return rc;
 }
 

@@ -247,3 +247,38 @@ def test_streamed_binding_refuses_device_layout_mixups():
         tla.ttt_write_streamed(K, K, theta, 0.1, 1, 16, 32)  # theta must be a device tensor
     with pytest.raises(ValueError):
         tla.ttt_read_streamed(K[:, ::2], theta, 16, 32, out=K[:, ::2])  # non-contiguous host tensor
+
+
+def test_wide_mlp_shape_rules(lib):
+    # the full-width 1024 -> 4096 -> 1024 MLP: one head, bf16, gradient descent
+    n, d, m = 5000, 1024, 4096
+    ws = lib.vggt3_ttt_workspace_bytes(n, 1, d, m, tla.BF16)
+    assert ws > 3 * d * m * 4  # holds at least the reduced gradient
+    assert lib.vggt3_ttt_workspace_bytes(n, 2, d, m, tla.BF16) == 0  # two heads: unsupported
+    assert lib.vggt3_ttt_workspace_bytes(n, 1, d, m, tla.F32) == 0  # no fp32 kernel
+    # the workspace stops growing once the scene exceeds one token chunk
+    big = lib.vggt3_ttt_workspace_bytes(10_000_000, 1, d, m, tla.BF16)
+    assert big == lib.vggt3_ttt_workspace_bytes(1_000_000, 1, d, m, tla.BF16)
+    assert big < 8 << 30
+    rws = lib.vggt3_ttt_read_workspace_bytes(n, 1, d, m, tla.BF16)
+    assert 0 < rws < ws
+    assert lib.vggt3_ttt_read_workspace_bytes(n, 16, 64, 128, tla.BF16) == 0  # per-head: none needed
+    big_ptr = ctypes.c_void_p(0x7000000000)
+    assert lib.vggt3_ttt_write(FAKE, FAKE2, FAKE3, n, 2, d, m, 0.1, 1, tla.BF16, big_ptr, ws, None,
+                               None) == tla.EUNSUPPORTED and "n_heads = 1" in _err(lib)
+    assert lib.vggt3_ttt_write_ex(FAKE, FAKE2, FAKE3, n, 1, d, m, 0.1, 1, tla.LOSS_DOT, tla.OPT_MUON, 5, tla.BF16,
+                                  big_ptr, ws, None, None) == tla.EUNSUPPORTED and "gradient descent" in _err(lib)
+    assert lib.vggt3_ttt_read(FAKE, FAKE3, FAKE2, n, 1, d, m, tla.BF16, None) == tla.EUNSUPPORTED
+    assert "vggt3_ttt_read_ex" in _err(lib)
+    assert lib.vggt3_ttt_read_ex(FAKE, FAKE3, FAKE2, n, 1, d, m, tla.BF16, None, 0, None) == tla.EWORKSPACE
+    assert lib.vggt3_ttt_read_ex(FAKE, FAKE3, FAKE2, n, 1, d, m, tla.BF16, big_ptr, rws - 1, None) == tla.EWORKSPACE
+    assert lib.vggt3_ttt_read_ex(FAKE, FAKE3, FAKE, n, 1, d, m, tla.BF16, big_ptr, rws, None) == tla.EINVAL
+    assert lib.vggt3_ttt_grad_partials(FAKE, FAKE2, FAKE3, n, 1, d, m, tla.BF16, big_ptr, ws,
+                                       None) == tla.EUNSUPPORTED
+    assert lib.vggt3_ttt_reduce(big_ptr, ws, n, 1, d, m, tla.BF16, 0, FAKE3, 0.1, None, None) == tla.EUNSUPPORTED
+    stage = lib.vggt3_ttt_stream_stage_bytes(4096, 1, d, tla.BF16)
+    assert lib.vggt3_ttt_write_streamed(FAKE, FAKE2, FAKE3, n, 1, d, m, 0.1, 1, 0, 0, 5, tla.BF16, 4096, big_ptr,
+                                        stage, big_ptr, ws, None, None, None) == tla.EUNSUPPORTED
+    # the workspace must not overlap the token inputs
+    assert lib.vggt3_ttt_grad(FAKE, FAKE2, FAKE3, big_ptr, 0, n, 1, d, m, tla.BF16, FAKE, ws, None,
+                              None) == tla.EINVAL

@@ -118,3 +118,39 @@ def test_wide_gradient_eq5_split_and_determinism():
     np.testing.assert_array_equal(bits(g), bits(g2))
     e = _per_matrix_err(to64(acc), to64(g))
     assert e.max() <= 1e-5, e
+
+
+def test_wide_views1000_chunked_gradient_and_sampled_read():
+    """The 1000-view scene (1,374,000 tokens: ten full 131,072-token chunks and a
+    ragged one). The gradient cannot be checked against the oracle at this
+    size; Eq. 5 fixes it instead: it must equal the sum of the gradients of two
+    halves cut off chunk boundaries (same per-token products, other fp32
+    summation order). The read is per token, so sampled rows are checked
+    against the oracle."""
+    cfg = _cfg(views=1000, steps=2)
+    print("[wide] views1000 gradient halves + sampled read", flush=True)
+    inp, Vp = _scene(cfg, with_q=True)
+    n = cfg.n_tokens
+    L = torch.empty(1, device=DEV)
+    g = tla.ttt_grad(inp.K, Vp, inp.theta0, 1, loss_out=L)
+    cut = 700_001
+    L2 = torch.empty(1, device=DEV)
+    acc = tla.ttt_grad(inp.K[:cut], Vp[:cut], inp.theta0, 1, loss_out=L2)
+    tla.ttt_grad(inp.K[cut:n], Vp[cut:n], inp.theta0, 1, grad=acc, accumulate=True, loss_out=L2)
+    torch.cuda.synchronize()
+    e = _per_matrix_err(to64(acc), to64(g))
+    print(f"  halves vs whole: per-matrix rel diff {e}", flush=True)
+    assert e.max() <= 1e-5, e
+    assert abs(L.item() - L2.item()) <= 1e-5 * abs(L.item())
+    assert torch.isfinite(g).all()
+    # read with a fitted theta: sampled tokens in several chunks, incl. the ragged tail
+    theta = inp.theta0.clone()
+    tla.ttt_write(inp.K, Vp, theta, cfg.lr, 2, 1)
+    O = tla.ttt_read(inp.Q, theta, 1)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.linspace(0, n - 1, 200).astype(np.int64), np.arange(n - 40, n),
+                                     131_070 + np.arange(6)]))
+    O_ref = oracle.ttt_read(to64(inp.Q[rows]), theta.cpu().numpy(), 1, D, M)
+    er = rel_err(to64(O[rows]), O_ref)
+    print(f"  sampled read rel err {er:.3e}", flush=True)
+    assert er <= TOL, er
