@@ -188,8 +188,9 @@ def wide_bench(args, loss_kind, opt_kind, recipe_desc):
     """The pages' full-width fast-weight MLP (one 1024 -> 4096 -> 1024 SwiGLU
     over the whole token) on the same scene: conv, `steps` write steps through
     vggt3_ttt_write_ex (a chunked sequence of bf16 MFMA GEMMs with fused
-    epilogues), read through vggt3_ttt_read_ex. The roofline is that of the
-    write's GEMM sequence as a whole: algorithmic flops over its event time."""
+    epilogues, then the GD or Muon update), read through vggt3_ttt_read_ex.
+    The roofline is that of the write's GEMM sequence as a whole: algorithmic
+    gradient flops over the write's event time (the Muon update included)."""
     import dataclasses
 
     import torch
@@ -324,10 +325,6 @@ def main():
     cfg = CONFIGS[args.config]
     loss_kind, opt_kind, recipe_desc = RECIPES[args.recipe]
     if args.mlp == "wide":
-        if opt_kind != "gd":
-            print("bench.py: the full-width MLP is written with gradient descent (--recipe mse_gd or dot_gd)",
-                  file=sys.stderr)
-            sys.exit(2)
         wide_bench(args, loss_kind, opt_kind, recipe_desc)
         return
     dev = torch.device("cuda:0")

@@ -156,9 +156,10 @@ size_t vggt3_ttt_workspace_bytes(int64_t n_tokens, int32_t n_heads, int32_t d_he
  * Supported (d_head, d_hidden): bf16 (64, 128); f32 (16, 32) and (64, 128);
  * and bf16 (1024, 4096) with n_heads = 1, the pages' full-width MLP ([GRAPH]
  * "TTT MLP Architecture and Inner Optimization": one 1024 -> 4096 -> 1024
- * SwiGLU), written with gradient descent (either loss). Its workspace holds
- * the intermediates of one chunk of up to 131,072 tokens (about 5.6 GB) plus
- * split-K gradient partials; its read needs vggt3_ttt_read_ex.
+ * SwiGLU), with either loss and either update (vggt3_ttt_write_ex). Its
+ * workspace holds the intermediates of one chunk of up to 131,072 tokens
+ * (about 5.6 GB), split-K gradient partials and the Newton-Schulz scratch;
+ * its read needs vggt3_ttt_read_ex.
  * n_tokens == 0 leaves theta unchanged (losses written as 0).
  */
 int vggt3_ttt_write(const void* K, const void* Vp, float* theta, int64_t n_tokens,
@@ -170,8 +171,9 @@ int vggt3_ttt_write(const void* K, const void* Vp, float* theta, int64_t n_token
  * vggt3_ttt_write with a choice of inner loss (VGGT3_LOSS_*) and update rule
  * (VGGT3_OPT_*); vggt3_ttt_write is the MSE / GD case. ns_steps (0 ..
  * VGGT3_MAX_NS_STEPS) is used only with VGGT3_OPT_MUON; loss_out receives the
- * chosen loss. Muon is supported for (d_head, d_hidden) = (64, 128) and
- * (16, 32). Other arguments, errors and n_tokens == 0 as in vggt3_ttt_write.
+ * chosen loss. Muon is supported for (d_head, d_hidden) = (64, 128), (16, 32)
+ * and (1024, 4096). Other arguments, errors and n_tokens == 0 as in
+ * vggt3_ttt_write.
  */
 int vggt3_ttt_write_ex(const void* K, const void* Vp, float* theta, int64_t n_tokens, int32_t n_heads,
                        int32_t d_head, int32_t d_hidden, float lr, int32_t steps, int32_t loss,
@@ -250,6 +252,24 @@ int vggt3_ttt_reduce(const void* workspace, size_t workspace_bytes, int64_t n_to
  */
 int vggt3_ttt_muon_apply(float* theta, const float* grad, float lr, int32_t n_heads, int32_t d_head,
                          int32_t d_hidden, int32_t ns_steps, void* stream);
+
+/*
+ * Bytes of device workspace vggt3_ttt_muon_apply_ex needs: 0 for the per-head
+ * shapes; for the full-width (1024, 4096) MLP (n_heads = 1) the fp32
+ * Newton-Schulz scratch (about 42 MB).
+ */
+size_t vggt3_ttt_muon_workspace_bytes(int32_t n_heads, int32_t d_head, int32_t d_hidden);
+
+/*
+ * vggt3_ttt_muon_apply with a workspace: the only Muon update of the
+ * full-width (1024, 4096) MLP (W_g and W_u are 1024 x 4096, W_d 4096 x 1024;
+ * the tall W_d is orthogonalised through A = X^T X, X <- a X + X B, the same
+ * map on its transpose). The products are fp32 GEMMs. For the per-head shapes
+ * the workspace is ignored. theta, grad and the workspace must not overlap.
+ */
+int vggt3_ttt_muon_apply_ex(float* theta, const float* grad, float lr, int32_t n_heads, int32_t d_head,
+                            int32_t d_hidden, int32_t ns_steps, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * One plain gradient-descent update theta <- theta - lr * grad over

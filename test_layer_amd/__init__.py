@@ -189,12 +189,24 @@ def ttt_grad_partials(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, n_
               _dtype_code(K), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
 
 
+def muon_workspace_bytes(n_heads: int, d_head: int, d_hidden: int) -> int:
+    return int(lib().vggt3_ttt_muon_workspace_bytes(n_heads, d_head, d_hidden))
+
+
 def ttt_muon_apply(theta: torch.Tensor, grad: torch.Tensor, lr: float, n_heads: int, d_head: int,
-                   d_hidden: int, ns_steps: int = 5) -> torch.Tensor:
-    """theta -= lr * NS(grad) per head and weight matrix (Muon update), in place."""
-    _check_dev(theta, grad)
-    _call("vggt3_ttt_muon_apply", _ptr(theta), _ptr(grad), float(lr), n_heads, d_head, d_hidden, int(ns_steps),
-          _stream())
+                   d_hidden: int, ns_steps: int = 5, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """theta -= lr * NS(grad) per head and weight matrix (Muon update), in place
+    (the full-width 1024 -> 4096 MLP takes a workspace)."""
+    _check_dev(theta, grad, workspace)
+    need = muon_workspace_bytes(n_heads, d_head, d_hidden)
+    if need == 0 and workspace is None:
+        _call("vggt3_ttt_muon_apply", _ptr(theta), _ptr(grad), float(lr), n_heads, d_head, d_hidden, int(ns_steps),
+              _stream())
+        return theta
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=theta.device)
+    _call("vggt3_ttt_muon_apply_ex", _ptr(theta), _ptr(grad), float(lr), n_heads, d_head, d_hidden, int(ns_steps),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
     return theta
 
 

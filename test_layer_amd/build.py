@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libvggt3.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "shortconv.hip", "ttt_write_bf16.hip", "ttt_read_bf16.hip", "ttt_f32.hip", "reduce.hip",
-           "muon.hip", "wide_mlp.hip"]
+           "muon.hip", "wide_mlp.hip", "wide_muon.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

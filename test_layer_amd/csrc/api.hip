@@ -98,11 +98,11 @@ WsLayout ws_layout(const MlpArgs& a, int P) {
 
 // Workspace of the wide MLP (write and read), for tokens processed in chunks
 // of at most wide::kChunk: bf16 GEMM operands of theta, the chunk's
-// intermediates, the split-K gradient partials, one reduced gradient and one
-// chunk's loss partials.
+// intermediates, the split-K gradient partials, one reduced gradient, one
+// chunk's loss partials and the Newton-Schulz scratch of the Muon update.
 struct WideWs {
   int64_t ct, ctp, nchunks, loss_stride;
-  size_t wgu, wdt, wdn, h, a, gp, dgu, y, pgu, pd, grad, loss, total, read_total;
+  size_t wgu, wdt, wdn, h, a, gp, dgu, y, pgu, pd, grad, loss, ns, total, read_total;
 };
 WideWs wide_ws(int64_t n) {
   namespace w = vggt3::wide;
@@ -132,6 +132,7 @@ WideWs wide_ws(int64_t n) {
   l.pd = take((size_t)w::kSplit * m * d * 4);
   l.grad = take(3 * d * m * 4);
   l.loss = take((size_t)l.loss_stride * 4);
+  l.ns = take(w::muon_workspace_floats(w::kD, w::kM) * 4);
   l.total = o;
   return l;
 }
@@ -419,11 +420,20 @@ int vggt3_ttt_write_ex(const void* K, const void* Vp, float* theta, int64_t n_to
     return ok();
   }
   if (is_wide(a.d, a.m)) {
-    if (optimizer != VGGT3_OPT_GD)
-      return fail(VGGT3_EUNSUPPORTED, "the %d -> %d -> %d MLP is written with gradient descent only", a.d, a.m, a.d);
+    const WideWs l = wide_ws(a.n);
+    char* base = static_cast<char*>(workspace);
+    float* gw = reinterpret_cast<float*>(base + l.grad);
     for (int st = 0; st < steps; ++st) {
-      rc = wide_grad(K, Vp, theta, a, loss, workspace, vggt3::kApply, theta, lr,
-                     loss_out ? loss_out + (size_t)st * n_heads : nullptr, 0, s);
+      float* lrow = loss_out ? loss_out + (size_t)st * n_heads : nullptr;
+      if (optimizer == VGGT3_OPT_GD) {
+        rc = wide_grad(K, Vp, theta, a, loss, workspace, vggt3::kApply, theta, lr, lrow, 0, s);
+      } else {
+        rc = wide_grad(K, Vp, theta, a, loss, workspace, vggt3::kStore, gw, 0.0f, lrow, 0, s);
+        if (!rc)
+          rc = check_hip(vggt3::wide::launch_muon(theta, gw, lr, a.d, a.m, ns_steps,
+                                                  reinterpret_cast<float*>(base + l.ns), s),
+                         "wide muon launch");
+      }
       if (rc) return rc;
     }
     return ok();
@@ -590,6 +600,36 @@ int vggt3_ttt_muon_apply(float* theta, const float* grad, float lr, int32_t n_he
   int rc = check_hip(vggt3::launch_muon_apply(theta, grad, lr, n_heads, d_head, d_hidden, ns_steps,
                                               static_cast<hipStream_t>(stream)),
                      "muon launch");
+  return rc ? rc : ok();
+}
+
+size_t vggt3_ttt_muon_workspace_bytes(int32_t n_heads, int32_t d_head, int32_t d_hidden) {
+  if (n_heads != 1 || !is_wide(d_head, d_hidden)) return 0;
+  return vggt3::wide::muon_workspace_floats(d_head, d_hidden) * sizeof(float);
+}
+
+int vggt3_ttt_muon_apply_ex(float* theta, const float* grad, float lr, int32_t n_heads, int32_t d_head,
+                            int32_t d_hidden, int32_t ns_steps, void* workspace, size_t workspace_bytes_,
+                            void* stream) {
+  if (!is_wide(d_head, d_hidden))
+    return vggt3_ttt_muon_apply(theta, grad, lr, n_heads, d_head, d_hidden, ns_steps, stream);
+  if (n_heads != 1) return fail(VGGT3_EUNSUPPORTED, "the %d -> %d MLP takes n_heads = 1", d_head, d_hidden);
+  if (ns_steps < 0 || ns_steps > VGGT3_MAX_NS_STEPS)
+    return fail(VGGT3_EINVAL, "ns_steps = %d outside [0, %d]", ns_steps, VGGT3_MAX_NS_STEPS);
+  if (!std::isfinite(lr)) return fail(VGGT3_EINVAL, "lr is not finite");
+  if (theta == nullptr || grad == nullptr) return fail(VGGT3_EINVAL, "theta or grad is NULL");
+  if (!aligned16(theta) || !aligned16(grad)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  const size_t need = vggt3_ttt_muon_workspace_bytes(n_heads, d_head, d_hidden);
+  if (workspace == nullptr) return fail(VGGT3_EWORKSPACE, "workspace is NULL, %zu bytes needed", need);
+  if (workspace_bytes_ < need) return fail(VGGT3_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_, need);
+  if (!aligned16(workspace)) return fail(VGGT3_EINVAL, "workspace is not 16-byte aligned");
+  const size_t tb = (size_t)3 * d_head * d_hidden * sizeof(float);
+  if (overlap(theta, tb, grad, tb) || overlap(workspace, workspace_bytes_, theta, tb) ||
+      overlap(workspace, workspace_bytes_, grad, tb))
+    return fail(VGGT3_EINVAL, "theta, grad and the workspace overlap");
+  int rc = check_hip(vggt3::wide::launch_muon(theta, grad, lr, d_head, d_hidden, ns_steps,
+                                              static_cast<float*>(workspace), static_cast<hipStream_t>(stream)),
+                     "wide muon launch");
   return rc ? rc : ok();
 }
 

@@ -60,5 +60,11 @@ hipError_t launch_reduce_partials(const float* p_gu, const float* p_d, int S, in
                                   float* dst, float lr, hipStream_t stream);
 hipError_t launch_sum(const float* x, int64_t n, float scale, int accumulate, float* out, hipStream_t stream);
 
+// Muon update theta -= lr * NS(grad) of the three matrices (fp32 GEMMs), with a
+// scratch of muon_workspace_floats(d, m) floats.
+size_t muon_workspace_floats(int d, int m);
+hipError_t launch_muon(float* theta, const float* grad, float lr, int d, int m, int ns_steps, float* ws,
+                       hipStream_t stream);
+
 }  // namespace wide
 }  // namespace vggt3

@@ -266,8 +266,8 @@ def test_wide_mlp_shape_rules(lib):
     big_ptr = ctypes.c_void_p(0x7000000000)
     assert lib.vggt3_ttt_write(FAKE, FAKE2, FAKE3, n, 2, d, m, 0.1, 1, tla.BF16, big_ptr, ws, None,
                                None) == tla.EUNSUPPORTED and "n_heads = 1" in _err(lib)
-    assert lib.vggt3_ttt_write_ex(FAKE, FAKE2, FAKE3, n, 1, d, m, 0.1, 1, tla.LOSS_DOT, tla.OPT_MUON, 5, tla.BF16,
-                                  big_ptr, ws, None, None) == tla.EUNSUPPORTED and "gradient descent" in _err(lib)
+    assert lib.vggt3_ttt_write_ex(FAKE, FAKE2, FAKE3, n, 1, d, m, 0.1, 1, tla.LOSS_DOT, tla.OPT_MUON, 99, tla.BF16,
+                                  big_ptr, ws, None, None) == tla.EINVAL and "ns_steps" in _err(lib)
     assert lib.vggt3_ttt_read(FAKE, FAKE3, FAKE2, n, 1, d, m, tla.BF16, None) == tla.EUNSUPPORTED
     assert "vggt3_ttt_read_ex" in _err(lib)
     assert lib.vggt3_ttt_read_ex(FAKE, FAKE3, FAKE2, n, 1, d, m, tla.BF16, None, 0, None) == tla.EWORKSPACE
@@ -279,6 +279,14 @@ def test_wide_mlp_shape_rules(lib):
     stage = lib.vggt3_ttt_stream_stage_bytes(4096, 1, d, tla.BF16)
     assert lib.vggt3_ttt_write_streamed(FAKE, FAKE2, FAKE3, n, 1, d, m, 0.1, 1, 0, 0, 5, tla.BF16, 4096, big_ptr,
                                         stage, big_ptr, ws, None, None, None) == tla.EUNSUPPORTED
+    mws = lib.vggt3_ttt_muon_workspace_bytes(1, d, m)
+    assert mws > 2 * d * m * 4 and lib.vggt3_ttt_muon_workspace_bytes(16, 64, 128) == 0
+    assert lib.vggt3_ttt_muon_apply(FAKE, FAKE2, 0.1, 1, d, m, 5, None) == tla.EUNSUPPORTED
+    assert lib.vggt3_ttt_muon_apply_ex(FAKE, FAKE2, 0.1, 1, d, m, 5, None, 0, None) == tla.EWORKSPACE
+    assert lib.vggt3_ttt_muon_apply_ex(FAKE, FAKE2, 0.1, 1, d, m, 5, big_ptr, mws - 4, None) == tla.EWORKSPACE
+    assert lib.vggt3_ttt_muon_apply_ex(FAKE, FAKE2, 0.1, 1, d, m, 70, big_ptr, mws, None) == tla.EINVAL
+    assert lib.vggt3_ttt_muon_apply_ex(FAKE, FAKE, 0.1, 1, d, m, 5, big_ptr, mws, None) == tla.EINVAL
+    assert lib.vggt3_ttt_muon_apply_ex(FAKE, FAKE2, 0.1, 2, d, m, 5, big_ptr, mws, None) == tla.EUNSUPPORTED
     # the workspace must not overlap the token inputs
     assert lib.vggt3_ttt_grad(FAKE, FAKE2, FAKE3, big_ptr, 0, n, 1, d, m, tla.BF16, FAKE, ws, None,
                               None) == tla.EINVAL

@@ -154,3 +154,62 @@ def test_wide_views1000_chunked_gradient_and_sampled_read():
     er = rel_err(to64(O[rows]), O_ref)
     print(f"  sampled read rel err {er:.3e}", flush=True)
     assert er <= TOL, er
+
+
+def _ns_gain(g, trials=2, eps=1e-3, seed=0):
+    """Largest observed ratio (relative change of NS(G)) / (relative change of
+    G) over random perturbations of the oracle's own gradient matrices (no GPU
+    value enters this)."""
+    r = np.random.default_rng(seed)
+    worst = 1.0
+    for G in oracle.split_theta(g.reshape(-1), D, M):
+        O = oracle.newton_schulz(G)
+        for _ in range(trials):
+            E = r.standard_normal(G.shape)
+            E *= eps * np.abs(G).max() / np.abs(E).max()
+            dO = oracle.newton_schulz(G + E) - O
+            worst = max(worst, (np.abs(dO).max() / np.abs(O).max()) / eps)
+    return worst
+
+
+def test_wide_write_dot_muon_parity():
+    """The pages' recipe at the pages' width: dot-product loss, Muon with 5
+    Newton-Schulz steps, 2 steps. Bar 2e-2 times the NS error gain, as for the
+    per-head Muon write."""
+    cfg = _cfg(steps=2)
+    print("[wide] dot + muon write", flush=True)
+    inp, Vp = _scene(cfg)
+    theta = inp.theta0.clone()
+    L = torch.empty((2, 1), device=DEV)
+    tla.ttt_write(inp.K, Vp, theta, cfg.lr, 2, 1, loss_out=L, loss="dot", optimizer="muon")
+    torch.cuda.synchronize()
+    th0 = inp.theta0.cpu().numpy()
+    K64, Vp_ref = to64(inp.K), _oracle_vp(inp)
+    th_ref, L_ref, grads = oracle.ttt_write(K64, Vp_ref, th0, 1, D, M, cfg.lr, 2, loss="dot", opt="muon")
+    kappa = _ns_gain(grads[0])
+    tol = TOL * kappa
+    ok, worst = dtheta_ok(theta.cpu().numpy().astype(np.float64), th_ref, th0, 1, tol, 2)
+    print(f"  NS gain {kappa:.2f}, dtheta worst/allowance {worst:.3f} (tol {tol:.3g})", flush=True)
+    assert ok, worst
+
+
+@pytest.mark.parametrize("ns_steps", [5, 2])
+def test_wide_muon_apply_parity(ns_steps):
+    """The Muon map alone on a seeded random gradient (fp32 GEMMs) against the
+    oracle's fp64 Newton-Schulz: 1e-4 normwise per matrix, as the per-head
+    Muon. One matrix gets a small norm, one a large one."""
+    gen = torch.Generator(device="cpu").manual_seed(300 + ns_steps)
+    theta = 0.02 * torch.randn((1, 3 * D * M), generator=gen)
+    grad = torch.randn((1, 3 * D * M), generator=gen)
+    grad[0, :D * M] *= 1e-3
+    grad[0, 2 * D * M:] *= 50.0
+    th_dev, g_dev = theta.to(DEV), grad.to(DEV)
+    ws = torch.empty(tla.muon_workspace_bytes(1, D, M), dtype=torch.uint8, device=DEV)
+    tla.ttt_muon_apply(th_dev, g_dev, 0.1, 1, D, M, ns_steps, workspace=ws)
+    torch.cuda.synchronize()
+    th0 = theta.numpy().astype(np.float64)
+    ref = oracle.muon_apply(th0, grad.numpy().astype(np.float64), 0.1, 1, D, M, ns_steps)
+    upd, upd_ref = th0 - th_dev.cpu().numpy().astype(np.float64), th0 - ref
+    e = _per_matrix_err(upd, upd_ref)
+    print(f"  wide muon apply ns{ns_steps} per-matrix rel err {e}", flush=True)
+    assert e.max() <= 1e-4, e
