@@ -131,7 +131,8 @@ WideWs wide_ws(int64_t n) {
   l.pgu = take((size_t)w::kSplit * d * 2 * m * 4);
   l.pd = take((size_t)w::kSplit * m * d * 4);
   l.grad = take(3 * d * m * 4);
-  l.loss = take((size_t)l.loss_stride * 4);
+  l.loss = take((size_t)(l.loss_stride > (int64_t)w::reduce_blocks(w::kD, w::kM) ? l.loss_stride
+                                                                                  : w::reduce_blocks(w::kD, w::kM)) * 4);
   l.ns = take(w::muon_workspace_floats(w::kD, w::kM) * 4);
   l.total = o;
   return l;
@@ -191,18 +192,17 @@ int wide_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& 
     g.M = nc; g.N = m; g.K = d; g.S = 1;
     if (dot) {
       g.nseg = 1; g.A[0] = Vc; g.lda[0] = d; g.B[0] = bf(l.wdn); g.ldb[0] = d;
-      g.in2 = bf(l.h); g.fout = lossc;
     } else {
       g.nseg = 2;
       g.A[0] = bf(l.y); g.lda[0] = d; g.A[1] = Vc; g.lda[1] = d;
       g.B[0] = bf(l.wdn); g.ldb[0] = d; g.B[1] = bf(l.wdn); g.ldb[1] = d;
     }
     g.in0 = bf(l.gp); g.in1 = bf(l.a); g.out0 = bf(l.dgu); g.ldo = 2 * m;
-    rc = check_hip(w::launch_gemm(dot ? w::EPI_DH_DOT : w::EPI_DH, g, s), "wide gemm P3");
+    rc = check_hip(w::launch_gemm(w::EPI_DH, g, s), "wide gemm P3");
     if (rc) return rc;
-    if (loss_out) {
-      // this chunk's per-workgroup loss sums (P2, or P3 for the dot loss)
-      const int64_t nt = (nc + w::kTile - 1) / w::kTile * ((dot ? m : d) / w::kTile);
+    if (loss_out && !dot) {
+      // this chunk's per-workgroup sums of (Y - V')^2 from P2
+      const int64_t nt = (nc + w::kTile - 1) / w::kTile * (d / w::kTile);
       rc = check_hip(w::launch_sum(lossc, nt, lscale, c > 0 ? 1 : loss_acc, loss_out, s), "loss sum launch");
       if (rc) return rc;
     }
@@ -231,8 +231,13 @@ int wide_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& 
     if (rc) return rc;
   }
   const float gscale = dot ? -1.0f : -2.0f / d;
-  rc = check_hip(w::launch_reduce_partials(f32(l.pgu), f32(l.pd), w::kSplit, d, m, gscale, (int)mode, dst, lr, s),
+  // dot loss = <W_d, gW_d> (theta read before the update)
+  float* wd_dot = (dot && loss_out) ? f32(l.loss) : nullptr;
+  rc = check_hip(w::launch_reduce_partials(f32(l.pgu), f32(l.pd), w::kSplit, d, m, gscale, (int)mode, dst, lr,
+                                           theta, wd_dot, s),
                  "wide reduce launch");
+  if (!rc && wd_dot)
+    rc = check_hip(w::launch_sum(wd_dot, w::reduce_blocks(d, m), 1.0f, loss_acc, loss_out, s), "loss sum launch");
   return rc;
 }
 

@@ -21,7 +21,6 @@ enum Epi {
   EPI_Y_LOSS = 2,    // Y -> -Y (row-major), sum (Y - V')^2 per workgroup
   EPI_Y_STORE = 3,   // Y -> O (row-major)
   EPI_DH = 4,        // D -> [D*GP | D*A] (row-major [rows][2m])
-  EPI_DH_DOT = 5,    // as EPI_DH, plus sum H*D per workgroup
   EPI_PARTIAL = 6    // fp32 split-K partial (C-native), stored or added
 };
 
@@ -47,7 +46,6 @@ struct GemmArgs {
   uint16_t* out2;
   const uint16_t* in0;
   const uint16_t* in1;
-  const uint16_t* in2;
   int64_t ldo, ldi;
   float* fout;
   int accumulate;
@@ -56,8 +54,11 @@ struct GemmArgs {
 hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t stream);
 hipError_t launch_pack(const float* theta, uint16_t* wgu, uint16_t* wdt, uint16_t* wdn, int d, int m,
                        hipStream_t stream);
+// Blocks of the partials reduction (one 256-thread block per 256 gradient
+// elements); with wd_dot it writes one W_d . g partial per block.
+constexpr unsigned reduce_blocks(int d, int m) { return (unsigned)((3 * (int64_t)d * m + 255) / 256); }
 hipError_t launch_reduce_partials(const float* p_gu, const float* p_d, int S, int d, int m, float scale, int mode,
-                                  float* dst, float lr, hipStream_t stream);
+                                  float* dst, float lr, const float* theta, float* wd_dot, hipStream_t stream);
 hipError_t launch_sum(const float* x, int64_t n, float scale, int accumulate, float* out, hipStream_t stream);
 
 // Muon update theta -= lr * NS(grad) of the three matrices (fp32 GEMMs), with a

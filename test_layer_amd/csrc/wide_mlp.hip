@@ -15,7 +15,9 @@
 //   P4  [gW_g | gW_u] += K^T [dG | dU],  gW_d += H^T (-Y) + H^T V'
 // so D = -(Y - V') W_d^T and all three accumulated gradients are the true
 // ones times -(d/2) (mean squared error) or -1 (dot-product loss, where
-// P2 is skipped and P3 is D = V' W_d^T). The residual is never rounded as a
+// P2 is skipped and P3 is D = V' W_d^T). The dot-product loss needs no
+// per-token work: -sum_i Y_i . V'_i = <W_d, -H^T V'> = <W_d, gW_d>, a dot
+// product of the weights with the reduced gradient (taken in the reduce). The residual is never rounded as a
 // whole: Y (small next to V' at the start of fitting) and V' enter as two
 // exact bf16 operands, as in the per-head write.
 //
@@ -320,8 +322,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
       const float s = block_sum(loss, red, tid);
       if (tid == 0) g.fout[t] = s;
     }
-  } else if constexpr (EPI == EPI_DH || EPI == EPI_DH_DOT) {
-    float loss = 0.0f;
+  } else if constexpr (EPI == EPI_DH) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -339,14 +340,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
           uint16_t* dst = g.out0 + row * g.ldo + col;
           dst[0] = f32_to_bf16_bits(dh * gv[r]);
           dst[g.N] = f32_to_bf16_bits(dh * av[r]);
-          if constexpr (EPI == EPI_DH_DOT)
-            if (ok) loss = fmaf(bf16_bits_to_f32(g.in2[row * g.N + col]), dh, loss);
         }
       }
-    }
-    if constexpr (EPI == EPI_DH_DOT) {
-      const float s = block_sum(loss, red, tid);
-      if (tid == 0) g.fout[t] = s;
     }
   } else if constexpr (EPI == EPI_PARTIAL) {
     float* dst = g.fout + (int64_t)slice * g.M * g.N;
@@ -417,12 +412,17 @@ __global__ __launch_bounds__(256) void pack_d_kernel(const float* __restrict__ t
 // Sum the S split-K partials (fixed pairwise tree) of the two gradient GEMMs
 // (C-native [d x 2m] = [gW_g | gW_u] and [m x d] = gW_d), scale, and apply to
 // theta / store / accumulate into grad in theta layout.
+// With wd_dot != NULL each block also writes, to wd_dot[block], the sum over
+// its W_d elements of theta_old * g (theta read before any update).
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ p_gu,
                                                               const float* __restrict__ p_d, int S, int d, int m,
                                                               float scale, int mode, float* __restrict__ dst,
-                                                              float lr) {
+                                                              float lr, const float* __restrict__ theta,
+                                                              float* __restrict__ wd_dot) {
+  __shared__ float red[4];
   const int64_t n_gu = 2 * (int64_t)d * m, n_all = 3 * (int64_t)d * m;
   const int64_t dm = (int64_t)d * m;
+  float dotv = 0.0f;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_all; i += (int64_t)gridDim.x * 256) {
     const bool gu = i < n_gu;
     const int64_t ci = gu ? i : i - n_gu;
@@ -445,12 +445,19 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __res
       ti = col < m ? row * m + col : dm + row * m + (col - m);
     else
       ti = 2 * dm + row * d + col;
+    if (wd_dot != nullptr && !gu) dotv = fmaf(theta[ti], gsum, dotv);
     if (mode == kApply)
       dst[ti] -= lr * gsum;
     else if (mode == kStore)
       dst[ti] = gsum;
     else
       dst[ti] += gsum;
+  }
+  if (wd_dot != nullptr) {
+    dotv = wave_sum(dotv);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dotv;
+    __syncthreads();
+    if (threadIdx.x == 0) wd_dot[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
   }
 }
 
@@ -479,7 +486,6 @@ hipError_t launch_gemm(int kind, const GemmArgs& g, hipStream_t stream) {
     case EPI_Y_LOSS: return launch_t<true, true, EPI_Y_LOSS>(g, stream);
     case EPI_Y_STORE: return launch_t<true, true, EPI_Y_STORE>(g, stream);
     case EPI_DH: return launch_t<true, true, EPI_DH>(g, stream);
-    case EPI_DH_DOT: return launch_t<true, true, EPI_DH_DOT>(g, stream);
     case EPI_PARTIAL: return launch_t<false, false, EPI_PARTIAL>(g, stream);
     default: return hipErrorInvalidValue;
   }
@@ -493,11 +499,9 @@ hipError_t launch_pack(const float* theta, uint16_t* wgu, uint16_t* wdt, uint16_
 }
 
 hipError_t launch_reduce_partials(const float* p_gu, const float* p_d, int S, int d, int m, float scale, int mode,
-                                  float* dst, float lr, hipStream_t stream) {
-  const int64_t n_all = 3 * (int64_t)d * m;
-  const unsigned blocks = (unsigned)((n_all + 255) / 256);
-  hipLaunchKernelGGL(reduce_partials_kernel, dim3(blocks), dim3(256), 0, stream, p_gu, p_d, S, d, m, scale, mode,
-                     dst, lr);
+                                  float* dst, float lr, const float* theta, float* wd_dot, hipStream_t stream) {
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3(reduce_blocks(d, m)), dim3(256), 0, stream, p_gu, p_d, S, d, m,
+                     scale, mode, dst, lr, theta, wd_dot);
   return hipGetLastError();
 }
 

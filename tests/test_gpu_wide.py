@@ -76,6 +76,15 @@ def test_wide_gradient_parity(loss):
     assert e.max() <= TOL, e
     if loss == "mse":
         assert le <= TOL, le
+    else:
+        # the dot loss is a sum of terms of either sign: its error is measured
+        # against the sum of the terms' magnitudes (oracle forward)
+        Wg, Wu, Wd = oracle.split_theta(th0.reshape(-1), D, M)
+        Y = oracle.swiglu_forward(to64(inp.K), Wg, Wu, Wd)["Y"]
+        scale = float(np.sum(np.abs(Y * _oracle_vp(inp))))
+        ld = abs(L.item() - L_ref[0]) / scale
+        print(f"  dot loss error / sum |Y V'| = {ld:.3e}", flush=True)
+        assert ld <= TOL, ld
 
 
 def test_wide_write_two_steps_parity():
