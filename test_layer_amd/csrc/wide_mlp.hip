@@ -45,6 +45,7 @@ constexpr int TSZ = 256 * BK;         // elements of one operand tile (32 KB)
 
 typedef __attribute__((address_space(3))) uint16_t lu16;
 typedef __attribute__((address_space(3))) u32x4 lu32x4;
+typedef __attribute__((address_space(3))) u32x2 lu32x2;
 typedef __attribute__((address_space(3))) void lvoid;
 
 __device__ __forceinline__ bf16x8 lop(const lu16* p) {
@@ -148,6 +149,40 @@ __device__ __forceinline__ int64_t cn_off(int64_t row0, int64_t col0, int64_t N,
   return ((row0 >> 4) * (N >> 4) + (col0 >> 4)) * 256 + lane * 4;
 }
 
+// Epilogue staging through LDS, one 18 KB region per wave (the GEMM tiles are
+// no longer needed then). An output sub-tile of 128 rows x (8 ncc) columns is
+// written transposed, [column][row] with a row pitch of EP_P elements, with
+// one 8-byte write per 4 consecutive rows of a column (the MFMA C layout), and
+// read back with the transpose read so that each lane holds 8 consecutive
+// columns of one row: 16-byte global stores instead of 2-byte ones.
+constexpr int EP_P = 144;
+constexpr int EP_ELEMS = 64 * EP_P;  // per wave
+constexpr int VP_P = 72;             // pitch of a wave's row-major [128][64] input tile
+static_assert(128 * VP_P <= EP_ELEMS, "input staging");
+constexpr int SMEM_ELEMS = NWAVE * EP_ELEMS > 4 * TSZ ? NWAVE * EP_ELEMS : 4 * TSZ;
+
+__device__ __forceinline__ void ep_put(lu16* T, int i, int j, int i16, int g4, float v0, float v1, float v2,
+                                       float v3) {
+  *(lu32x2*)(T + (16 * j + i16) * EP_P + 16 * i + 4 * g4) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+}
+
+// Rows row0 + 0..127 (those below r_end) of columns col0 + 0 .. 8*NCC-1 from
+// the staged tile T to dst (row-major, leading dimension ld).
+template <int NCC>
+__device__ __forceinline__ void ep_flush(const lu16* T, uint16_t* dst, int64_t ld, int64_t row0, int64_t col0,
+                                         int64_t r_end, int lane) {
+  const int s = lane & 15, gq = lane >> 4, j = s >> 2, q = s & 3;
+#pragma unroll
+  for (int p = 0; p < 8 * NCC / 4; ++p) {
+    const int c0 = NCC == 8 ? 16 * (p >> 1) : 16 * p;
+    const int cc = NCC == 8 ? 4 * (p & 1) + gq : gq;
+    const lu16* a = T + (8 * cc + j) * EP_P + c0 + 4 * q;
+    const u32x2 lo = ltr(a), hi = ltr(a + 4 * EP_P);
+    const int64_t row = row0 + c0 + s;
+    if (row < r_end) st16(dst + row * ld + col0 + 8 * cc, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  }
+}
+
 __device__ __forceinline__ float block_sum(float v, float* red, int tid) {
   v = wave_sum(v);
   __syncthreads();
@@ -198,7 +233,7 @@ template <bool AKC, bool BKC, int EPI>
 __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   // Two stages of (A, B) tiles: A of stage s at s * TSZ, B at (2 + s) * TSZ,
   // so that a stage's tiles are 64 KB apart and the other stage's 32 KB.
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TSZ];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM_ELEMS];
   lu16* const A0 = (lu16*)smem;
   lu16* const A1 = A0 + TSZ;
   lu16* const B0 = A0 + 2 * TSZ;
@@ -261,7 +296,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   const int i16e = lane_e & 15, g4e = lane_e >> 4;
   const int64_t rbase = m0 + wm * WM + 4 * g4e;  // + 16 i + r
   const int64_t cbase = n0 + wn * WN + i16e;     // + 16 j
-  float* red = (float*)smem;                    // LDS is free after the loop
+  float* red = (float*)smem;
+  __syncthreads();  // every wave is done with the operand tiles
+  lu16* const T = A0 + wid * EP_ELEMS;  // this wave's staging region
+  const int64_t wrow0 = m0 + wm * WM;    // this wave's first row
 
   if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_H) {
     // Columns are interleaved in blocks of 64: [G of 32 units | U of the same
@@ -278,71 +316,87 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
           const float s = sigmoid_fast(gg);
           const float a = gg * s;
           const float h = a * uu;
-          hv[r] = h;
+          // Rows past M (up to the tile boundary) are stored as zeros: the
+          // token-reduction GEMMs read them as the zero operand of their tail.
+          hv[r] = rbase + 16 * i + r < g.M ? h : 0.0f;
           av[r] = a;
           gv[r] = fmaf(-h, s, fmaf(uu, s, h));
         }
-        const int64_t hid = hid0 + 16 * j + i16e;
-        const int64_t row = rbase + 16 * i;
-        // Rows past M (up to the tile boundary) are written as zeros: the
-        // token-reduction GEMMs read them as the zero operand of their tail.
-#pragma unroll
-        for (int r = 0; r < 4; ++r) g.out0[(row + r) * g.ldo + hid] = f32_to_bf16_bits(row + r < g.M ? hv[r] : 0.0f);
+        ep_put(T, i, j, i16e, g4e, hv[0], hv[1], hv[2], hv[3]);
         if constexpr (EPI == EPI_SWIGLU) {
-          const int64_t o = cn_off(m0 + wm * WM + 16 * i, hid0 + 16 * j, g.ldo, lane_e);
+          const int64_t o = cn_off(wrow0 + 16 * i, hid0 + 16 * j, g.ldo, lane_e);
           st8(g.out1 + o, u32x2{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])});
           st8(g.out2 + o, u32x2{pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])});
         }
       }
     }
+    ep_flush<4>(T, g.out0, g.ldo, wrow0, hid0, EPI == EPI_SWIGLU ? wrow0 + 128 : g.M, lane_e);
   } else if constexpr (EPI == EPI_Y_LOSS || EPI == EPI_Y_STORE) {
     float loss = 0.0f;
+    if constexpr (EPI == EPI_Y_LOSS) {
+      // V' for this wave's 128 x 64 outputs: 16-byte loads into LDS (row-major),
+      // then one transpose read per 16x16 tile gives each lane its 4 rows.
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+      for (int it = 0; it < 16; ++it) {
+        const int qd = it * 64 + lane_e, r = qd >> 3, cc = qd & 7;
+        int64_t row = wrow0 + r;
+        row = row < g.M ? row : g.M - 1;
+        const u32x4 v = ld16(g.in0 + row * g.ldi + n0 + wn * WN + 8 * cc);
+        *(lu32x4*)(T + r * VP_P + 8 * cc) = v;
+      }
+      const int jr4 = i16e >> 2, q4e = i16e & 3;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t col = cbase + 16 * j;
+      for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t row = rbase + 16 * i + r;
-          if (row < g.M) {
-            const float y = acc[i][j][r];
-            if constexpr (EPI == EPI_Y_LOSS) {
-              const float rr = y - bf16_bits_to_f32(g.in0[row * g.ldi + col]);
-              loss = fmaf(rr, rr, loss);
-              g.out0[row * g.ldo + col] = f32_to_bf16_bits(-y);
-            } else {
-              g.out0[row * g.ldo + col] = f32_to_bf16_bits(y);
-            }
+        for (int j = 0; j < TN; ++j) {
+          const u32x2 vv = ltr(T + (16 * i + 4 * g4e + jr4) * VP_P + 16 * j + 4 * q4e);
+          const float v[4] = {bf16_lo(vv[0]), bf16_hi(vv[0]), bf16_lo(vv[1]), bf16_hi(vv[1])};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float rr = acc[i][j][r] - v[r];
+            if (rbase + 16 * i + r < g.M) loss = fmaf(rr, rr, loss);
           }
         }
       }
     }
+    const float sg = EPI == EPI_Y_LOSS ? -1.0f : 1.0f;  // P2 stores -Y
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        ep_put(T, i, j, i16e, g4e, sg * acc[i][j][0], sg * acc[i][j][1], sg * acc[i][j][2], sg * acc[i][j][3]);
+    ep_flush<8>(T, g.out0, g.ldo, wrow0, n0 + wn * WN, g.M, lane_e);
     if constexpr (EPI == EPI_Y_LOSS) {
       const float s = block_sum(loss, red, tid);
       if (tid == 0) g.fout[t] = s;
     }
   } else if constexpr (EPI == EPI_DH) {
+    // [dG | dU] = [D * GP | D * A], rows past M stored as zeros (see EPI_SWIGLU).
+    float dv[TM][TN][4];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int64_t col = cbase + 16 * j;  // hidden unit
-        const int64_t o = cn_off(m0 + wm * WM + 16 * i, n0 + wn * WN + 16 * j, g.N, lane_e);
+        const int64_t o = cn_off(wrow0 + 16 * i, n0 + wn * WN + 16 * j, g.N, lane_e);
         const u32x2 ap = ld8(g.in1 + o), gp = ld8(g.in0 + o);
         const float av[4] = {bf16_lo(ap[0]), bf16_hi(ap[0]), bf16_lo(ap[1]), bf16_hi(ap[1])};
         const float gv[4] = {bf16_lo(gp[0]), bf16_hi(gp[0]), bf16_lo(gp[1]), bf16_hi(gp[1])};
+        float dg[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int64_t row = rbase + 16 * i + r;
-          const bool ok = row < g.M;  // rows past M: zeros (see EPI_SWIGLU)
-          const float dh = ok ? acc[i][j][r] : 0.0f;
-          uint16_t* dst = g.out0 + row * g.ldo + col;
-          dst[0] = f32_to_bf16_bits(dh * gv[r]);
-          dst[g.N] = f32_to_bf16_bits(dh * av[r]);
+          const float dh = rbase + 16 * i + r < g.M ? acc[i][j][r] : 0.0f;
+          dg[r] = dh * gv[r];
+          dv[i][j][r] = dh * av[r];
         }
+        ep_put(T, i, j, i16e, g4e, dg[0], dg[1], dg[2], dg[3]);
       }
     }
+    ep_flush<8>(T, g.out0, g.ldo, wrow0, n0 + wn * WN, wrow0 + 128, lane_e);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) ep_put(T, i, j, i16e, g4e, dv[i][j][0], dv[i][j][1], dv[i][j][2], dv[i][j][3]);
+    ep_flush<8>(T, g.out0 + g.N, g.ldo, wrow0, n0 + wn * WN, wrow0 + 128, lane_e);
   } else if constexpr (EPI == EPI_PARTIAL) {
     float* dst = g.fout + (int64_t)slice * g.M * g.N;
 #pragma unroll
