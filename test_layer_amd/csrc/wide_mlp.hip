@@ -251,7 +251,20 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   const int64_t b = xcd_remap(blockIdx.x, (int64_t)gridDim.x);
   const int slice = (int)(b / tiles);
   const int64_t t = b % tiles;
-  const int64_t m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
+  // Tiles in groups of 4 row tiles x all column tiles, column-fastest within a
+  // group: the workgroups that run together on one XCD (xcd_remap gives each
+  // XCD a contiguous range) share 4 A row panels and a few B column panels in
+  // its L2 instead of streaming every B panel.
+  int64_t tm_, tn_;
+  {
+    constexpr int64_t GM = 4;
+    const int64_t group = t / (GM * tiles_n), first = group * GM;
+    const int64_t gsz = tiles_m - first < GM ? tiles_m - first : GM;
+    const int64_t in = t % (GM * tiles_n);
+    tm_ = first + in % gsz;
+    tn_ = in / gsz;
+  }
+  const int64_t m0 = tm_ * BM, n0 = tn_ * BN;
 
   const int64_t nkb = (g.K + BK - 1) / BK;
   const int64_t kb0 = nkb * slice / g.S, kb1 = nkb * (slice + 1) / g.S;
