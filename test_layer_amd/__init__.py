@@ -238,13 +238,12 @@ def ttt_read(Q: torch.Tensor, theta: torch.Tensor, n_heads: int, d_hidden: Optio
     d, m = _mlp_dims(theta, Q, n_heads, d_hidden)
     dt = _dtype_code(Q)
     need = read_workspace_bytes(Q.shape[0], n_heads, d, m, dt)
-    if need == 0 and workspace is None:
-        _call("vggt3_ttt_read", _ptr(Q), _ptr(theta), _ptr(out), Q.shape[0], n_heads, d, m, dt, _stream())
-        return out
-    if workspace is None:
+    if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    _call("vggt3_ttt_read_ex", _ptr(Q), _ptr(theta), _ptr(out), Q.shape[0], n_heads, d, m, dt, _ptr(workspace),
-          workspace.numel() * workspace.element_size(), _stream())
+    nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    # vggt3_ttt_read_ex serves every shape (the per-head ones ignore the workspace)
+    _call("vggt3_ttt_read_ex", _ptr(Q), _ptr(theta), _ptr(out), Q.shape[0], n_heads, d, m, dt, _ptr(workspace), nb,
+          _stream())
     return out
 
 

@@ -251,7 +251,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   const int64_t b = xcd_remap(blockIdx.x, (int64_t)gridDim.x);
   const int slice = (int)(b / tiles);
   const int64_t t = b % tiles;
-  // Tiles in groups of 4 row tiles x all column tiles, column-fastest within a
+  // Tiles in groups of 4 row tiles x all column tiles, row-fastest within a
   // group: the workgroups that run together on one XCD (xcd_remap gives each
   // XCD a contiguous range) share 4 A row panels and a few B column panels in
   // its L2 instead of streaming every B panel.

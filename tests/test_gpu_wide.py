@@ -222,3 +222,38 @@ def test_wide_muon_apply_parity(ns_steps):
     e = _per_matrix_err(upd, upd_ref)
     print(f"  wide muon apply ns{ns_steps} per-matrix rel err {e}", flush=True)
     assert e.max() <= 1e-4, e
+
+
+@pytest.mark.parametrize("n", [1, 7, 255, 257])
+def test_wide_tiny_and_ragged_token_counts(n):
+    """Token counts below one tile, and one either side of a 256-row tile
+    boundary: gradient, loss and read against the oracle."""
+    cfg = _cfg()
+    inp, Vp = _scene(cfg, with_q=True)
+    K, V, Q = inp.K[:n].contiguous(), Vp[:n].contiguous(), inp.Q[:n].contiguous()
+    L = torch.empty(1, device=DEV)
+    g = tla.ttt_grad(K, V, inp.theta0, 1, loss_out=L)
+    theta = inp.theta0 * 10.0
+    O = tla.ttt_read(Q, theta, 1)
+    torch.cuda.synchronize()
+    th0 = inp.theta0.cpu().numpy()
+    Vp_ref = _oracle_vp(inp)[:n]
+    g_ref, L_ref = oracle.ttt_grad(to64(K), Vp_ref, th0, 1, D, M)
+    e = _per_matrix_err(to64(g), g_ref)
+    assert e.max() <= TOL, (n, e)
+    assert abs(L.item() - L_ref[0]) <= TOL * abs(L_ref[0])
+    O_ref = oracle.ttt_read(to64(Q), theta.cpu().numpy(), 1, D, M)
+    assert rel_err(to64(O), O_ref) <= TOL
+
+
+def test_wide_empty_scene():
+    theta = (0.02 * torch.randn((1, 3 * D * M))).to(DEV)
+    before = theta.clone()
+    empty = torch.empty((0, D), dtype=torch.bfloat16, device=DEV)
+    L = torch.full((2, 1), 5.0, device=DEV)
+    tla.ttt_write(empty, empty, theta, 0.1, 2, 1, loss_out=L, loss="dot", optimizer="muon")
+    g = tla.ttt_grad(empty, empty, theta, 1)
+    O = tla.ttt_read(empty, theta, 1)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(theta), bits(before))
+    assert torch.all(L == 0) and torch.all(g == 0) and O.shape == (0, D)
