@@ -28,6 +28,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+SPEC_CLOCK_GHZ = 2.4
+# Shader clock under the gradient kernel, from the committed counter run
+# (profiles/ttt_layer_views1000_counters.md): GPU-active cycles counted at the
+# 2.4 GHz spec (3.411 ms) against the kernel's traced duration (4.215 ms).
+COUNTER_CLOCK_GHZ = round(SPEC_CLOCK_GHZ * 3.411 / 4.215, 2)
 PEAK_HBM_GBS = 8000.0
 METRIC = "TTT-layer tokens/sec (write+read) at 1000 views; % bf16 MFMA peak"
 GRAD_KERNEL = "grad_partial_bf16_kernel"
@@ -275,6 +280,8 @@ def wide_bench(args, loss_kind, opt_kind, recipe_desc):
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
+            "clock_GHz_from_counters": COUNTER_CLOCK_GHZ,
+            "frac_at_counter_clock": achieved / (PEAK_BF16_TFLOPS * COUNTER_CLOCK_GHZ / SPEC_CLOCK_GHZ),
             "traffic": None,
             "avg_launch_ms": write_ms / cfg.steps,
             "flops_per_launch": fw * n,
@@ -441,6 +448,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
+            "clock_GHz_from_counters": COUNTER_CLOCK_GHZ,
+            "frac_at_counter_clock": achieved / (PEAK_BF16_TFLOPS * COUNTER_CLOCK_GHZ / SPEC_CLOCK_GHZ),
             "traffic": load_traffic(args.recipe),
             "avg_launch_ms": grad_avg_ms,
             "flops_per_launch": grad_flops,
