@@ -292,6 +292,8 @@ def wide_bench(args, loss_kind, opt_kind, recipe_desc):
         "read_TFLOPs": fr * inp.Q.shape[0] / (read_ms * 1e-3) / 1e12,
         "final_loss": float(loss[-1, 0].item()),
     }
+    if args.offload > 0:
+        res["offload"] = offload_bench(tla, inp, Vp, cfg, args, loss_kind, opt_kind)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, cfg, loss=loss_kind, opt=opt_kind)
     print(json.dumps(res), flush=True)

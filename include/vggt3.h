@@ -353,6 +353,9 @@ size_t vggt3_ttt_stream_stage_bytes(int64_t chunk_tokens, int32_t n_heads, int32
  *                    copies (NULL or equal to stream serialises them).
  * theta, stage, workspace and loss_out must not overlap. The gradient equals
  * vggt3_ttt_grad called with accumulate on each chunk in turn, bit for bit.
+ * The full-width (1, 1024, 4096) MLP is supported too (workspace sized for
+ * one chunk the same way; chunks of at most 131,072 tokens keep that workspace
+ * at its smallest).
  * Errors as in vggt3_ttt_write_ex; a HIP runtime error part-way through
  * returns VGGT3_EHIP with part of the work enqueued.
  */
@@ -380,6 +383,18 @@ int vggt3_ttt_read_streamed(const void* Q_host, const float* theta, void* O_host
                             int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t dtype,
                             int64_t chunk_tokens, void* stage, size_t stage_bytes, void* stream,
                             void* h2d_stream, void* d2h_stream);
+
+/*
+ * vggt3_ttt_read_streamed with a device workspace of at least
+ * vggt3_ttt_read_workspace_bytes(min(chunk_tokens, n_tokens), ...) bytes: the
+ * streamed read of the full-width (1024, 4096) MLP. For the per-head shapes
+ * the workspace is ignored (and may be NULL). It must not overlap stage or
+ * theta.
+ */
+int vggt3_ttt_read_streamed_ex(const void* Q_host, const float* theta, void* O_host, int64_t n_tokens,
+                               int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t dtype,
+                               int64_t chunk_tokens, void* stage, size_t stage_bytes, void* workspace,
+                               size_t workspace_bytes, void* stream, void* h2d_stream, void* d2h_stream);
 
 #ifdef __cplusplus
 }

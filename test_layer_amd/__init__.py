@@ -327,7 +327,8 @@ def ttt_write_streamed(K_host: torch.Tensor, Vp_host: torch.Tensor, theta: torch
 def ttt_read_streamed(Q_host: torch.Tensor, theta: torch.Tensor, n_heads: int, chunk_tokens: int,
                       d_hidden: Optional[int] = None, out: Optional[torch.Tensor] = None,
                       stage: Optional[torch.Tensor] = None, h2d_stream: Optional[torch.cuda.Stream] = None,
-                      d2h_stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+                      d2h_stream: Optional[torch.cuda.Stream] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """O = T_theta(Q) for host-resident Q, written to a host tensor (query mode
     over a frozen theta), streamed in chunks of `chunk_tokens`. `out` defaults
     to a new pinned tensor; read it after synchronising the current stream."""
@@ -345,7 +346,13 @@ def ttt_read_streamed(Q_host: torch.Tensor, theta: torch.Tensor, n_heads: int, c
         h2d_stream = _side_stream(theta.device, "h2d")
     if d2h_stream is None:
         d2h_stream = _side_stream(theta.device, "d2h")
-    _call("vggt3_ttt_read_streamed", _ptr(Q_host), _ptr(theta), _ptr(out), n, n_heads, d, m, dt, int(chunk_tokens),
-          _ptr(stage), stage.numel() * stage.element_size(), _stream(), ctypes.c_void_p(h2d_stream.cuda_stream),
-          ctypes.c_void_p(d2h_stream.cuda_stream))
+    if workspace is None:
+        need = read_workspace_bytes(ct, n_heads, d, m, dt)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=theta.device)
+    _check_dev(workspace)
+    nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("vggt3_ttt_read_streamed_ex", _ptr(Q_host), _ptr(theta), _ptr(out), n, n_heads, d, m, dt,
+          int(chunk_tokens), _ptr(stage), stage.numel() * stage.element_size(), _ptr(workspace), nb, _stream(),
+          ctypes.c_void_p(h2d_stream.cuda_stream), ctypes.c_void_p(d2h_stream.cuda_stream))
     return out

@@ -56,6 +56,8 @@ SIGNATURES = {
                                          c_void_p, c_void_p, c_void_p]),
     "vggt3_ttt_read_streamed": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_int, c_int, c_int, c_int, c_i64,
                                         c_void_p, c_size, c_void_p, c_void_p, c_void_p]),
+    "vggt3_ttt_read_streamed_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_int, c_int, c_int, c_int, c_i64,
+                                           c_void_p, c_size, c_void_p, c_size, c_void_p, c_void_p, c_void_p]),
 }
 
 _lib = None

@@ -152,10 +152,13 @@ size_t workspace_bytes(const MlpArgs& a, int* P_out) {
 // One gradient pass of the wide MLP over all n tokens at theta: the gradient
 // (times `scale` inside the reduce) goes to dst in `mode` (apply with lr,
 // store, accumulate); the loss to loss_out (stored, or added if loss_acc).
+// `l` is the workspace layout (wide_ws of the largest token count the
+// workspace was sized for, >= a.n); tokens are taken in chunks of l.ct.
 int wide_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& a, int32_t loss, void* ws,
-              vggt3::ReduceMode mode, float* dst, float lr, float* loss_out, int loss_acc, hipStream_t s) {
+              const WideWs& l, vggt3::ReduceMode mode, float* dst, float lr, float* loss_out, int loss_acc,
+              hipStream_t s) {
   namespace w = vggt3::wide;
-  const WideWs l = wide_ws(a.n);
+  const int64_t nchunks = (a.n + l.ct - 1) / l.ct;
   char* base = static_cast<char*>(ws);
   auto bf = [&](size_t off) { return reinterpret_cast<uint16_t*>(base + off); };
   auto f32 = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
@@ -166,7 +169,7 @@ int wide_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& 
   const float lscale = dot ? -1.0f : 1.0f / d;
   const uint16_t* Kb = static_cast<const uint16_t*>(K);
   const uint16_t* Vb = static_cast<const uint16_t*>(Vp);
-  for (int64_t c = 0; c < l.nchunks; ++c) {
+  for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t t0 = c * l.ct, nc = a.n - t0 < l.ct ? a.n - t0 : l.ct;
     const uint16_t* Kc = Kb + t0 * d;
     const uint16_t* Vc = Vb + t0 * d;
@@ -242,15 +245,16 @@ int wide_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& 
 }
 
 // Read of the wide MLP: per chunk, H = SwiGLU(Q) then O = H W_d.
-int wide_read(const void* Q, const float* theta, void* O, const MlpArgs& a, void* ws, hipStream_t s) {
+int wide_read(const void* Q, const float* theta, void* O, const MlpArgs& a, void* ws, const WideWs& l,
+              hipStream_t s) {
   namespace w = vggt3::wide;
-  const WideWs l = wide_ws(a.n);
+  const int64_t nchunks = (a.n + l.ct - 1) / l.ct;
   char* base = static_cast<char*>(ws);
   auto bf = [&](size_t off) { return reinterpret_cast<uint16_t*>(base + off); };
   const int d = w::kD, m = w::kM;
   int rc = check_hip(w::launch_pack(theta, bf(l.wgu), bf(l.wdt), bf(l.wdn), d, m, s), "pack launch");
   if (rc) return rc;
-  for (int64_t c = 0; c < l.nchunks; ++c) {
+  for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t t0 = c * l.ct, nc = a.n - t0 < l.ct ? a.n - t0 : l.ct;
     w::GemmArgs g{};
     g.M = nc; g.N = 2 * m; g.K = d; g.nseg = 1; g.S = 1;
@@ -431,9 +435,9 @@ int vggt3_ttt_write_ex(const void* K, const void* Vp, float* theta, int64_t n_to
     for (int st = 0; st < steps; ++st) {
       float* lrow = loss_out ? loss_out + (size_t)st * n_heads : nullptr;
       if (optimizer == VGGT3_OPT_GD) {
-        rc = wide_grad(K, Vp, theta, a, loss, workspace, vggt3::kApply, theta, lr, lrow, 0, s);
+        rc = wide_grad(K, Vp, theta, a, loss, workspace, l, vggt3::kApply, theta, lr, lrow, 0, s);
       } else {
-        rc = wide_grad(K, Vp, theta, a, loss, workspace, vggt3::kStore, gw, 0.0f, lrow, 0, s);
+        rc = wide_grad(K, Vp, theta, a, loss, workspace, l, vggt3::kStore, gw, 0.0f, lrow, 0, s);
         if (!rc)
           rc = check_hip(vggt3::wide::launch_muon(theta, gw, lr, a.d, a.m, ns_steps,
                                                   reinterpret_cast<float*>(base + l.ns), s),
@@ -502,8 +506,8 @@ int vggt3_ttt_grad_ex(const void* K, const void* Vp, const float* theta, float* 
     return ok();
   }
   if (is_wide(a.d, a.m))
-    rc = wide_grad(K, Vp, theta, a, loss, workspace, accumulate ? vggt3::kAccum : vggt3::kStore, grad, 0.0f,
-                   loss_out, accumulate ? 1 : 0, s);
+    rc = wide_grad(K, Vp, theta, a, loss, workspace, wide_ws(a.n), accumulate ? vggt3::kAccum : vggt3::kStore, grad,
+                   0.0f, loss_out, accumulate ? 1 : 0, s);
   else
     rc = run_grad(K, Vp, theta, a, workspace, P, loss, accumulate ? vggt3::kAccum : vggt3::kStore, grad, 0.0f,
                   loss_out, s);
@@ -696,7 +700,7 @@ int vggt3_ttt_read_ex(const void* Q, const float* theta, void* O, int64_t n_toke
     return fail(VGGT3_EINVAL, "O overlaps Q, theta or the workspace");
   if (overlap(workspace, workspace_bytes_, Q, xb) || overlap(workspace, workspace_bytes_, theta, tb))
     return fail(VGGT3_EINVAL, "workspace overlaps Q or theta");
-  rc = wide_read(Q, theta, O, a, workspace, static_cast<hipStream_t>(stream));
+  rc = wide_read(Q, theta, O, a, workspace, wide_ws(a.n), static_cast<hipStream_t>(stream));
   return rc ? rc : ok();
 }
 
@@ -719,12 +723,10 @@ int vggt3_ttt_write_streamed(const void* K_host, const void* Vp_host, float* the
     return fail(VGGT3_EINVAL, "unknown optimizer %d", optimizer);
   if (optimizer == VGGT3_OPT_MUON && (ns_steps < 0 || ns_steps > VGGT3_MAX_NS_STEPS))
     return fail(VGGT3_EINVAL, "ns_steps = %d outside [0, %d]", ns_steps, VGGT3_MAX_NS_STEPS);
-  if (optimizer == VGGT3_OPT_MUON && !((d_head == 64 && d_hidden == 128) || (d_head == 16 && d_hidden == 32)))
-    return fail(VGGT3_EUNSUPPORTED, "no Muon kernel for d_head = %d, d_hidden = %d", d_head, d_hidden);
   if (!std::isfinite(lr)) return fail(VGGT3_EINVAL, "lr is not finite");
   if (steps < 1) return fail(VGGT3_EINVAL, "steps = %d < 1", steps);
   if (chunk_tokens < 1) return fail(VGGT3_EINVAL, "chunk_tokens = %lld < 1", (long long)chunk_tokens);
-  if (is_wide(a.d, a.m)) return fail(VGGT3_EUNSUPPORTED, "no streamed write for the %d -> %d MLP", a.d, a.m);
+  const bool wide = is_wide(a.d, a.m);
   if (theta == nullptr) return fail(VGGT3_EINVAL, "theta is NULL");
   if (!aligned16(theta) || (loss_out && !aligned16(loss_out)))
     return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
@@ -758,13 +760,15 @@ int vggt3_ttt_write_streamed(const void* K_host, const void* Vp_host, float* the
 
   // The accumulated gradient sits where the workspace layout of a full chunk
   // puts its reduced gradient; a shorter last chunk has no more partials
-  // (ttt_num_chunks grows with n), so its partials end before it.
-  float* gacc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_layout(ca, P).grad);
+  // (ttt_num_chunks grows with n), so its partials end before it. The
+  // full-width MLP uses its layout for the chunk capacity throughout.
+  const WideWs wl = wide_ws(ct);
+  float* gacc = reinterpret_cast<float*>(static_cast<char*>(workspace) + (wide ? wl.grad : ws_layout(ca, P).grad));
   const int64_t nc = (a.n + ct - 1) / ct;
   const int64_t tail = a.n - (nc - 1) * ct;
-  if (ws_layout(MlpArgs{tail, n_heads, d_head, d_hidden, dtype},
-                vggt3::ttt_num_chunks(tail, n_heads, tile_tokens(dtype)))
-          .grad > ws_layout(ca, P).grad)
+  if (!wide && ws_layout(MlpArgs{tail, n_heads, d_head, d_hidden, dtype},
+                         vggt3::ttt_num_chunks(tail, n_heads, tile_tokens(dtype)))
+                       .grad > ws_layout(ca, P).grad)
     return fail(VGGT3_EUNSUPPORTED, "internal: tail chunk layout exceeds the workspace");
 
   hipStream_t cs = copy_stream ? static_cast<hipStream_t>(copy_stream) : s;
@@ -806,13 +810,21 @@ int vggt3_ttt_write_streamed(const void* K_host, const void* Vp_host, float* the
         if (rc) return rc;
       }
       const MlpArgs ta{tn, n_heads, d_head, d_hidden, dtype};
-      rc = run_grad(Kd, Vd, theta, ta, workspace, vggt3::ttt_num_chunks(tn, n_heads, tile_tokens(dtype)), loss,
-                    c == 0 ? vggt3::kStore : vggt3::kAccum, gacc, 0.0f, lrow, s);
+      if (wide)
+        rc = wide_grad(Kd, Vd, theta, ta, loss, workspace, wl, c == 0 ? vggt3::kStore : vggt3::kAccum, gacc, 0.0f,
+                       lrow, c > 0 ? 1 : 0, s);
+      else
+        rc = run_grad(Kd, Vd, theta, ta, workspace, vggt3::ttt_num_chunks(tn, n_heads, tile_tokens(dtype)), loss,
+                      c == 0 ? vggt3::kStore : vggt3::kAccum, gacc, 0.0f, lrow, s);
       if (!rc && cs != s) rc = check_hip(hipEventRecord(freed[sl], s), "event record");
       if (rc) return rc;
     }
     if (optimizer == VGGT3_OPT_GD)
       rc = check_hip(vggt3::launch_apply(theta, gacc, lr, (int64_t)tb / 4, s), "apply launch");
+    else if (wide)
+      rc = check_hip(vggt3::wide::launch_muon(theta, gacc, lr, d_head, d_hidden, ns_steps,
+                                              reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ns), s),
+                     "wide muon launch");
     else
       rc = check_hip(vggt3::launch_muon_apply(theta, gacc, lr, n_heads, d_head, d_hidden, ns_steps, s),
                      "muon launch");
@@ -821,15 +833,15 @@ int vggt3_ttt_write_streamed(const void* K_host, const void* Vp_host, float* the
   return ok();
 }
 
-int vggt3_ttt_read_streamed(const void* Q_host, const float* theta, void* O_host, int64_t n_tokens,
-                            int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t dtype,
-                            int64_t chunk_tokens, void* stage, size_t stage_bytes, void* stream,
-                            void* h2d_stream, void* d2h_stream) {
+int vggt3_ttt_read_streamed_ex(const void* Q_host, const float* theta, void* O_host, int64_t n_tokens,
+                               int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t dtype, int64_t chunk_tokens,
+                               void* stage, size_t stage_bytes, void* workspace, size_t workspace_bytes_,
+                               void* stream, void* h2d_stream, void* d2h_stream) {
   const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
   int rc = check_mlp(a);
   if (rc) return rc;
   if (chunk_tokens < 1) return fail(VGGT3_EINVAL, "chunk_tokens = %lld < 1", (long long)chunk_tokens);
-  if (is_wide(a.d, a.m)) return fail(VGGT3_EUNSUPPORTED, "no streamed read for the %d -> %d MLP", a.d, a.m);
+  const bool wide = is_wide(a.d, a.m);
   if (a.n == 0) return ok();
   if (Q_host == nullptr || theta == nullptr || O_host == nullptr) return fail(VGGT3_EINVAL, "NULL pointer");
   if (!aligned16(theta)) return fail(VGGT3_EINVAL, "theta is not 16-byte aligned");
@@ -842,6 +854,16 @@ int vggt3_ttt_read_streamed(const void* Q_host, const float* theta, void* O_host
   if (stage_bytes < need) return fail(VGGT3_EWORKSPACE, "stage has %zu bytes, %zu needed", stage_bytes, need);
   if (!aligned16(stage)) return fail(VGGT3_EINVAL, "stage is not 16-byte aligned");
   if (overlap(theta, theta_bytes(a), stage, stage_bytes)) return fail(VGGT3_EINVAL, "stage overlaps theta");
+  const WideWs wl = wide_ws(ct);
+  if (wide) {
+    if (workspace == nullptr) return fail(VGGT3_EWORKSPACE, "workspace is NULL, %zu bytes needed", wl.read_total);
+    if (workspace_bytes_ < wl.read_total)
+      return fail(VGGT3_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_, wl.read_total);
+    if (!aligned16(workspace)) return fail(VGGT3_EINVAL, "workspace is not 16-byte aligned");
+    if (overlap(workspace, workspace_bytes_, stage, stage_bytes) ||
+        overlap(workspace, workspace_bytes_, theta, theta_bytes(a)))
+      return fail(VGGT3_EINVAL, "workspace overlaps stage or theta");
+  }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipStream_t hs = h2d_stream ? static_cast<hipStream_t>(h2d_stream) : s;
@@ -886,10 +908,14 @@ int vggt3_ttt_read_streamed(const void* Q_host, const float* theta, void* O_host
     if (!rc && c >= 2 && ds != s) rc = check_hip(hipStreamWaitEvent(s, o_out[sl], 0), "stream wait");
     if (rc) return rc;
     const int64_t tn = chunk_len(c);
-    hipError_t e = dtype == VGGT3_BF16 ? vggt3::launch_read_bf16(q_slot(c), theta, o_slot(c), tn, n_heads, s)
-                                       : vggt3::launch_read_f32(q_slot(c), theta, o_slot(c), tn, n_heads, d_head,
-                                                                d_hidden, s);
-    rc = check_hip(e, "read kernel launch");
+    if (wide) {
+      rc = wide_read(q_slot(c), theta, o_slot(c), MlpArgs{tn, n_heads, d_head, d_hidden, dtype}, workspace, wl, s);
+    } else {
+      hipError_t e = dtype == VGGT3_BF16 ? vggt3::launch_read_bf16(q_slot(c), theta, o_slot(c), tn, n_heads, s)
+                                         : vggt3::launch_read_f32(q_slot(c), theta, o_slot(c), tn, n_heads, d_head,
+                                                                  d_hidden, s);
+      rc = check_hip(e, "read kernel launch");
+    }
     if (!rc) rc = check_hip(hipEventRecord(done[sl], s), "event record");
     if (!rc && ds != s) rc = check_hip(hipStreamWaitEvent(ds, done[sl], 0), "stream wait");
     if (!rc)
@@ -906,6 +932,14 @@ int vggt3_ttt_read_streamed(const void* Q_host, const float* theta, void* O_host
     if (rc) return rc;
   }
   return ok();
+}
+
+int vggt3_ttt_read_streamed(const void* Q_host, const float* theta, void* O_host, int64_t n_tokens,
+                            int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t dtype,
+                            int64_t chunk_tokens, void* stage, size_t stage_bytes, void* stream,
+                            void* h2d_stream, void* d2h_stream) {
+  return vggt3_ttt_read_streamed_ex(Q_host, theta, O_host, n_tokens, n_heads, d_head, d_hidden, dtype, chunk_tokens,
+                                    stage, stage_bytes, nullptr, 0, stream, h2d_stream, d2h_stream);
 }
 
 }  // extern "C"

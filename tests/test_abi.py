@@ -277,8 +277,18 @@ def test_wide_mlp_shape_rules(lib):
                                        None) == tla.EUNSUPPORTED
     assert lib.vggt3_ttt_reduce(big_ptr, ws, n, 1, d, m, tla.BF16, 0, FAKE3, 0.1, None, None) == tla.EUNSUPPORTED
     stage = lib.vggt3_ttt_stream_stage_bytes(4096, 1, d, tla.BF16)
+    ws_chunk = lib.vggt3_ttt_workspace_bytes(4096, 1, d, m, tla.BF16)
     assert lib.vggt3_ttt_write_streamed(FAKE, FAKE2, FAKE3, n, 1, d, m, 0.1, 1, 0, 0, 5, tla.BF16, 4096, big_ptr,
-                                        stage, big_ptr, ws, None, None, None) == tla.EUNSUPPORTED
+                                        stage, ctypes.c_void_p(0x7800000000), ws_chunk - 1, None, None,
+                                        None) == tla.EWORKSPACE
+    rws_chunk = lib.vggt3_ttt_read_workspace_bytes(4096, 1, d, m, tla.BF16)
+    assert lib.vggt3_ttt_read_streamed_ex(FAKE, FAKE3, FAKE2, n, 1, d, m, tla.BF16, 4096, big_ptr, stage, None, 0,
+                                          None, None, None) == tla.EWORKSPACE
+    assert lib.vggt3_ttt_read_streamed_ex(FAKE, FAKE3, FAKE2, n, 1, d, m, tla.BF16, 4096, big_ptr, stage,
+                                          ctypes.c_void_p(0x7800000000), rws_chunk - 2, None, None,
+                                          None) == tla.EWORKSPACE
+    assert lib.vggt3_ttt_read_streamed(FAKE, FAKE3, FAKE2, n, 1, d, m, tla.BF16, 4096, big_ptr, stage, None, None,
+                                       None) == tla.EWORKSPACE
     mws = lib.vggt3_ttt_muon_workspace_bytes(1, d, m)
     assert mws > 2 * d * m * 4 and lib.vggt3_ttt_muon_workspace_bytes(16, 64, 128) == 0
     assert lib.vggt3_ttt_muon_apply(FAKE, FAKE2, 0.1, 1, d, m, 5, None) == tla.EUNSUPPORTED

@@ -230,3 +230,41 @@ def test_views1000_streamed_write_and_read_bitwise():
     O = tla.ttt_read_streamed(_pinned(inp.Q), theta, cfg.n_heads, chunk)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits(O), bits(O_ref))
+
+
+# ---------------------------------------------------------------------------
+# the full-width 1024 -> 4096 -> 1024 MLP streamed from host memory
+# ---------------------------------------------------------------------------
+
+
+def _wide_cfg(views=2, steps=2):
+    return replace(CONFIGS["views24"], n_views=views, n_heads=1, d_head=1024, d_hidden=4096, steps=steps,
+                   name=f"wide_stream{views}v")
+
+
+@pytest.mark.parametrize("recipe", [("mse", "gd"), ("dot", "muon")], ids=["mse_gd", "dot_muon"])
+def test_wide_write_streamed_equals_chunked_grad_bitwise(recipe):
+    """2 views (2,748 tokens) in chunks of 1,000: three chunks through the two
+    slots, the last ragged; each chunk's gradient is the full-width GEMM pass."""
+    loss, opt = recipe
+    cfg = _wide_cfg()
+    print(f"[stream] wide write {loss}/{opt}", flush=True)
+    inp, Vp = _scene(cfg)
+    ref_theta, ref_losses = _chunked_reference(inp.K, Vp, inp.theta0, cfg, 1000, loss, opt)
+    theta = inp.theta0.clone()
+    losses = torch.empty((cfg.steps, 1), device=DEV)
+    tla.ttt_write_streamed(_pinned(inp.K), _pinned(Vp), theta, cfg.lr, cfg.steps, 1, 1000, loss_out=losses,
+                           loss=loss, optimizer=opt)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(theta), bits(ref_theta))
+    np.testing.assert_array_equal(bits(losses), bits(ref_losses))
+
+
+def test_wide_read_streamed_equals_read_bitwise():
+    cfg = _wide_cfg()
+    inp = make_inputs(cfg, DEV, with_q=True)
+    theta = inp.theta0 * 10.0
+    ref = tla.ttt_read(inp.Q, theta, 1)
+    out = tla.ttt_read_streamed(_pinned(inp.Q), theta, 1, 1000)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(out), bits(ref))
