@@ -6,22 +6,41 @@
 // flattened again; per its Appendix A note, camera and register tokens bypass
 // the conv. The conv is depthwise (one 3x3 filter per channel), zero padded.
 //
-// Design (HBM-bound stencil). A work item is one (view, column x, segment of
-// SEG rows, block of up to 256 4-channel groups); a few workgroups per CU walk
-// the items with a grid stride (loading the filters once), and thread t owns
-// channel group 256*block + t. Everything that decides which taps exist (x at
-// a grid edge, the segment touching the top or bottom row) is therefore
-// uniform across the workgroup: the left/right edges select a template
-// instance, and rows outside the grid become scalar branches that skip those
-// taps instead of selecting zeros per element. Each thread issues the loads of
-// all SEG+2 input rows of its segment at columns x-1, x, x+1 at once (8 bytes
-// each; about 23 KB in flight per wave, which is what keeps HBM busy) from a
-// uniform row address plus its 32-bit lane offset, then computes the SEG
-// output rows with a rotating 3x3 window of fp32 vectors in registers. Lanes of
-// a wave cover consecutive channel groups of one token (512 contiguous bytes
-// per wave access); the x-1 / x+1 re-reads of neighbouring columns hit L1/L2,
-// and workgroups are remapped so that each XCD walks a contiguous range of
-// columns.
+// Design (HBM-bound stencil). Two kernels share one arithmetic contract.
+//
+// shortconv_lds_kernel (bf16, 3x3, channels a multiple of 64, grid rows up to
+// 126 columns): an LDS-haloed stencil. A workgroup walks strips (view, block of
+// 64 channels) down the grid in blocks of 3 output rows. LDS holds a ring of 10
+// staged input rows [slot][column][64 channels] (bf16, 128 bytes per token)
+// with a zero column on each side; every block brings in the rows it needs that
+// are not staged yet (a strip's first block: the zero row above the grid and
+// rows 0..3; later blocks: the next 3 rows, or the zero row below the grid) with
+// direct global -> LDS loads (global_load_lds_dwordx4, one 64-lane instruction
+// per 1 KB of a row), so each input row is read from HBM once. Those loads for
+// block k + 1 are issued before block k is computed and fill ring slots block k
+// does not read: one barrier per block, and the loads overlap the arithmetic.
+// Thread (q, x) computes channel quad q of column x with a rotating 3x3 window
+// of LDS reads; 16 lanes cover a token's 128 bytes, so LDS reads and the
+// output stores are contiguous. The grid is a multiple of the channel-block
+// count, so a workgroup's strips share one channel block and it loads its
+// filters once.
+//
+// shortconv_kernel (everything else: fp32, wider grids, other channel counts):
+// a work item is one (view, column x, segment of SEG rows, block of up to 256
+// 4-channel groups); a few workgroups per CU walk the items with a grid stride
+// (loading the filters once), and thread t owns channel group 256*block + t.
+// Everything that decides which taps exist (x at a grid edge, the segment
+// touching the top or bottom row) is therefore uniform across the workgroup:
+// the left/right edges select a template instance, and rows outside the grid
+// become scalar branches that skip those taps instead of selecting zeros per
+// element. Each thread issues the loads of all SEG+2 input rows of its segment
+// at columns x-1, x, x+1 at once (8 bytes each; about 23 KB in flight per
+// wave) from a uniform row address plus its 32-bit lane offset, then computes
+// the SEG output rows with a rotating 3x3 window of fp32 vectors in registers.
+// Lanes of a wave cover consecutive channel groups of one token (512 contiguous
+// bytes per wave access); the x-1 / x+1 re-reads of neighbouring columns hit
+// L1/L2, and workgroups are remapped so that each XCD walks a contiguous range
+// of columns.
 //
 // Bit-exact contract: acc = +0; taps with the row offset outermost and the
 // column offset innermost; acc = fl(acc + fl(w*v)), never fused (this file is
@@ -29,7 +48,8 @@
 // v = 0; the result is rounded to bf16 with ties to even. An out-of-grid tap
 // adds fl(w*0) = +-0 to an accumulator that is never -0 (it starts at +0 and a
 // round-to-nearest sum is -0 only if both terms are), which leaves it
-// unchanged, so such taps are skipped.
+// unchanged, so shortconv_kernel skips such taps and shortconv_lds_kernel
+// multiplies the staged zeros: both give the same bits for finite filters.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -277,6 +297,171 @@ __global__ __launch_bounds__(256) void shortconv_kxk_kernel(const char* __restri
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// LDS-haloed form (bf16, 3x3); see the file header.
+constexpr int LDS_CB = 64;         // channels per strip (128 bytes per token)
+constexpr int LDS_R = 3;           // output rows per block
+constexpr int LDS_NS = 2 * LDS_R + 4;  // ring slots
+constexpr int LDS_NT = 256;        // threads per workgroup
+constexpr int LDS_WG_PER_CU = 3;   // 3 x 49.9 KB of LDS at 37 columns
+constexpr size_t LDS_MAX_BYTES = 160 * 1024;
+
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Ring bookkeeping: each block "introduces" rows into the next free slots (in
+// order). Block 0 of a strip introduces the zero row -1 and rows 0 .. R (R + 2
+// slots), block b > 0 rows bR+1 .. bR+R (R slots; rows past the grid are not
+// loaded, and the row just below the grid is zeroed when it is among them).
+// A block's R + 2 input rows bR-1 .. bR+R are then consecutive slots starting
+// at `start` (its first introduced slot for b = 0, two before it otherwise);
+// the next block's rows go to the R + 2 slots after them, which this block does
+// not read. That needs 2R + 4 slots.
+__global__ __launch_bounds__(LDS_NT) void shortconv_lds_kernel(const uint16_t* __restrict__ V,
+                                                              uint16_t* __restrict__ Vp, const float* __restrict__ w,
+                                                              int64_t n_strips, int grid_h, int grid_w, int n_special,
+                                                              int C, int n_cb, int pieces_per_row) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t ring[];
+  constexpr int CB = LDS_CB, R = LDS_R, NS = LDS_NS, NT = LDS_NT;
+  constexpr int NQ = CB / 4;   // 4-channel quads per token
+  constexpr int NCH = CB / 8;  // 16-byte chunks per token
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int W2 = grid_w + 2;
+  const int row_chunks = grid_w * NCH;
+  const int n_blk = (grid_h + R - 1) / R;
+  const int64_t tpv = (int64_t)n_special + (int64_t)grid_h * grid_w;
+  const int64_t G = gridDim.x;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+  for (int i = tid; i < NS * 2 * NCH; i += NT) {  // the side columns of every slot stay zero
+    const int slot = i / (2 * NCH), side = (i / NCH) & 1, c = i % NCH;
+    *reinterpret_cast<u32x4*>(ring + (slot * W2 + (side ? W2 - 1 : 0)) * CB + 8 * c) = z4;
+  }
+
+  auto introduce = [&](int64_t strip, int b, int first) {
+    const int cb = (int)(strip % n_cb);
+    const int64_t tok0 = (strip / n_cb) * tpv;
+    if (b == 0) {  // special tokens pass through (before any direct load is in flight)
+      for (int i = tid; i < n_special * NCH; i += NT) {
+        const int64_t o = (tok0 + i / NCH) * C + (int64_t)cb * CB + 8 * (i % NCH);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(V + o), reinterpret_cast<u32x4*>(Vp + o));
+      }
+    }
+    const int y_new = b == 0 ? 0 : b * R + 1;
+    const int want = b == 0 ? R + 1 : R;
+    int n_new = grid_h - y_new < want ? grid_h - y_new : want;
+    if (n_new < 0) n_new = 0;
+    int s_new = b == 0 ? first + 1 : first;  // slot of row y_new
+    if (s_new >= NS) s_new -= NS;
+    const uint16_t* src = V + (tok0 + n_special + (int64_t)y_new * grid_w) * C + (int64_t)cb * CB;
+    // wave instruction i of n_new * pieces_per_row loads piece i % ppr (64 chunks) of row i / ppr
+    int row = 0, k = wid;
+    while (k >= pieces_per_row) {
+      k -= pieces_per_row;
+      ++row;
+    }
+    while (row < n_new) {
+      int slot = s_new + row;
+      if (slot >= NS) slot -= NS;
+      const int j = k * 64 + lane;  // chunk of the row: token j / NCH, 16-byte part j % NCH
+      if (j < row_chunks) {
+        const uint16_t* g = src + ((int64_t)row * grid_w + j / NCH) * C + 8 * (j % NCH);
+        __builtin_amdgcn_global_load_lds(g, (lds_void*)((lds_u16*)ring + (slot * W2 + 1) * CB + k * 512), 16, 0,
+                                         0);
+      }
+      k += NW;
+      while (k >= pieces_per_row) {
+        k -= pieces_per_row;
+        ++row;
+      }
+    }
+    if (b == 0)  // row -1
+      for (int i = tid; i < row_chunks; i += NT) *reinterpret_cast<u32x4*>(ring + (first * W2 + 1) * CB + 8 * i) = z4;
+    if (grid_h >= y_new && grid_h < y_new + want) {  // row grid_h
+      int slot = s_new + (grid_h - y_new);
+      if (slot >= NS) slot -= NS;
+      for (int i = tid; i < row_chunks; i += NT) *reinterpret_cast<u32x4*>(ring + (slot * W2 + 1) * CB + 8 * i) = z4;
+    }
+  };
+
+  int64_t s_cur = xcd_remap(blockIdx.x, G);
+  if (s_cur >= n_strips) return;
+  const int q = tid % NQ;
+  float wt[9][4];
+  {
+    const int cb = (int)(s_cur % n_cb);  // the same for all strips s_cur + k G
+#pragma unroll
+    for (int t = 0; t < 9; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wt[t][j] = w[(int64_t)(cb * CB + 4 * q + j) * 9 + t];
+  }
+
+  auto compute = [&](int64_t strip, int b, int start) {
+    const int cb = (int)(strip % n_cb);
+    const int y0 = b * R;
+    const int rows = grid_h - y0 < R ? grid_h - y0 : R;
+    uint16_t* ob = Vp + ((strip / n_cb) * tpv + n_special + (int64_t)y0 * grid_w) * C + (int64_t)cb * CB + 4 * q;
+    for (int x = tid / NQ; x < grid_w; x += NT / NQ) {
+      const uint16_t* col = ring + x * CB + 4 * q;  // staged column x holds input column x - 1
+      float win[3][3][4];  // win[k % 3][dx]: input row y0 - 1 + k, columns x - 1 .. x + 1
+      auto fetch = [&](int k, int dst) {
+        int slot = start + k;
+        if (slot >= NS) slot -= NS;
+#pragma unroll
+        for (int dx = 0; dx < 3; ++dx)
+          ConvTraits<true>::widen(*reinterpret_cast<const u32x2*>(col + (slot * W2 + dx) * CB), win[dst][dx]);
+      };
+      fetch(0, 0);
+      fetch(1, 1);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (r >= rows) break;
+        fetch(r + 2, (r + 2) % 3);
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int dy = 0; dy < 3; ++dy)
+#pragma unroll
+          for (int dx = 0; dx < 3; ++dx)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float p = wt[3 * dy + dx][j] * win[(r + dy) % 3][dx][j];
+              acc[j] = acc[j] + p;
+            }
+        __builtin_nontemporal_store(ConvTraits<true>::narrow(acc),
+                                    reinterpret_cast<u32x2*>(ob + ((int64_t)r * grid_w + x) * C));
+      }
+    }
+  };
+
+  int b_cur = 0, first_cur = 0;
+  introduce(s_cur, 0, first_cur);
+  int first_next = R + 2;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  while (true) {
+    int64_t s_next = s_cur;
+    int b_next = b_cur + 1;
+    if (b_next == n_blk) {
+      b_next = 0;
+      s_next = s_cur + G;
+    }
+    const bool more = s_next < n_strips;
+    if (more) introduce(s_next, b_next, first_next);
+    compute(s_cur, b_cur, b_cur == 0 ? first_cur : (first_cur + NS - 2) % NS);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's direct loads have landed
+    __syncthreads();
+    if (!more) break;
+    first_cur = first_next;
+    first_next = (first_next + (b_next == 0 ? R + 2 : R)) % NS;
+    s_cur = s_next;
+    b_cur = b_next;
+  }
+}
+
+size_t lds_ring_bytes(int grid_w) { return (size_t)LDS_NS * (grid_w + 2) * LDS_CB * 2; }
+
 }  // namespace
 
 hipError_t launch_shortconv_k(const void* V, void* Vp, const float* w, int64_t n_views, int grid_h, int grid_w,
@@ -310,6 +495,27 @@ hipError_t launch_shortconv(const void* V, void* Vp, const float* w, int64_t n_v
   // so the filters are loaded once per workgroup rather than once per item.
   const int64_t max_grid = (int64_t)VGGT3_CONV_WG_PER_CU * 256;
   const unsigned n_blocks = (unsigned)(n_work < max_grid ? n_work : max_grid);
+  const size_t ring_bytes = lds_ring_bytes(grid_w);
+  if (bf16 && C % LDS_CB == 0 && ring_bytes <= LDS_MAX_BYTES) {
+    bool ok = true;
+    if (ring_bytes > 64 * 1024)
+      ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&shortconv_lds_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)ring_bytes) == hipSuccess;
+    if (ok) {
+      const int n_cb = C / LDS_CB;
+      const int64_t n_strips = n_views * n_cb;
+      // a multiple of n_cb, so that the strips s, s + G, ... of a workgroup share a channel block
+      int64_t g = (int64_t)LDS_WG_PER_CU * 256 / n_cb;
+      g = (g < 1 ? 1 : g) * n_cb;
+      if (g > n_strips) g = n_strips;
+      const int pieces_per_row = (grid_w * (LDS_CB / 8) + 63) / 64;
+      hipLaunchKernelGGL(shortconv_lds_kernel, dim3((unsigned)g), dim3(LDS_NT), ring_bytes, stream,
+                         static_cast<const uint16_t*>(V), static_cast<uint16_t*>(Vp), w, n_strips, grid_h, grid_w,
+                         n_special, C, n_cb, pieces_per_row);
+      return hipGetLastError();
+    }
+    (void)hipGetLastError();
+  }
   if (bf16)
     hipLaunchKernelGGL(shortconv_kernel<true>, dim3(n_blocks), dim3(256), 0, stream, static_cast<const char*>(V),
                        static_cast<char*>(Vp), w, n_work, grid_h, grid_w, n_special, C, n_seg, n_cblk);

@@ -63,6 +63,14 @@ CONV_CASES = [
     (1, 1, 1, 1, 1, 8, "bf16"),
     (4, 3, 2, 0, 2, 4, "f32"),
     (2, 37, 37, 5, 4, 64, "f32"),
+    # bf16, 64-channel multiples, rows up to 126 columns: the LDS ring kernel
+    (2, 9, 126, 1, 1, 64, "bf16"),  # widest grid row that fits LDS (160 KB)
+    (2, 7, 40, 3, 3, 64, "bf16"),   # three channel blocks
+    (5, 4, 4, 2, 1, 64, "bf16"),    # a ragged last block of rows
+    (3, 1, 9, 0, 1, 64, "bf16"),    # a single grid row
+    # bf16 outside it: the register-window kernel
+    (1, 4, 127, 0, 1, 64, "bf16"),  # grid row too wide for the LDS ring
+    (1, 2, 3, 0, 3, 32, "bf16"),    # 96 channels
 ]
 
 
@@ -94,6 +102,23 @@ def test_shortconv_special_tokens_and_edges_bitexact():
     Vp = _conv(inp)
     ref = _oracle_conv(inp, "f32")
     np.testing.assert_array_equal(bits(Vp), f32_to_bits(ref, False))
+
+
+def test_shortconv_bf16_extreme_values_bitexact():
+    """The LDS ring kernel on signed zeros, subnormal products and large magnitudes (bf16 range)."""
+    from dataclasses import replace
+    cfg = replace(CONFIGS["tiny_f32"], n_views=3, grid_h=7, grid_w=5, n_special=2, n_heads=2, d_head=64,
+                  d_hidden=128, dtype="bf16", normalize=True, name="conv-edge-bf16")
+    inp = make_inputs(cfg, DEV, with_q=False)
+    V = inp.V.float()
+    V[::3] *= 1e-38  # subnormal inputs and products
+    V[1::7] = -0.0
+    V[2::5] *= 1e30
+    inp.V.copy_(V.to(torch.bfloat16))
+    Vp = _conv(inp)
+    torch.cuda.synchronize()
+    ref = _oracle_conv(inp, "bf16")
+    np.testing.assert_array_equal(bits(Vp), f32_to_bits(ref, True))
 
 
 # ----------------------------------------------------------------------------
