@@ -61,10 +61,12 @@ def source_sha256(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic(recipe="mse_gd"):
+def load_traffic(recipe="mse_gd", config="views1000"):
     """HBM bytes per launch of the gradient kernel from the committed rocprofv3
-    counter summary, or None if absent or taken on different kernel source."""
-    path = TRAFFIC_FILE if recipe == "mse_gd" else TRAFFIC_FILE.replace("_views1000", f"_{recipe}_views1000")
+    counter summary of this recipe and workload, or None if there is none or it
+    was taken on different kernel source."""
+    tag = config if recipe == "mse_gd" else f"{recipe}_{config}"
+    path = TRAFFIC_FILE.replace("_views1000", f"_{tag}")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -321,8 +323,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; multi-GPU runs (--gpus > 1) are not "
-              "supported (the layer's data-parallel sharding is described in DESIGN.md only).",
+        print("bench.py: runs on exactly one GPU; multi-GPU runs (--gpus > 1) are not supported "
+              "(the layer's data-parallel sharding is a design only, with no multi-GPU code).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -452,7 +454,7 @@ def main():
             "frac": achieved / PEAK_BF16_TFLOPS,
             "clock_GHz_from_counters": COUNTER_CLOCK_GHZ,
             "frac_at_counter_clock": achieved / (PEAK_BF16_TFLOPS * COUNTER_CLOCK_GHZ / SPEC_CLOCK_GHZ),
-            "traffic": load_traffic(args.recipe),
+            "traffic": load_traffic(args.recipe, cfg.name),
             "avg_launch_ms": grad_avg_ms,
             "flops_per_launch": grad_flops,
         },
