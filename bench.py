@@ -315,6 +315,9 @@ def main():
                     help="fast-weight MLP: 16 per-head SwiGLUs 64 -> 128 -> 64 (default) or the pages' full-width "
                          "1024 -> 4096 -> 1024 SwiGLU")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--with-loss", action="store_true",
+                    help="compute the inner-loss value in every timed write step (as vggt3_ttt_write with a "
+                         "loss_out does); by default it is computed once, after timing")
     ap.add_argument("--offload", type=int, default=0, metavar="CHUNK",
                     help="also time the offloaded step (K, V', Q in pinned host memory, streamed through the GPU in "
                          "CHUNK-token chunks; O streamed back) and report it under 'offload' (never as value)")
@@ -361,6 +364,11 @@ def main():
     gbuf = torch.empty_like(theta)
     nq = inp.Q.shape[0]
 
+    # The timed step computes what vggt3_ttt_write(loss_out = NULL) computes: the
+    # inner-loss value is a diagnostic the layer does not need (--with-loss
+    # times it too). One untimed step with the loss follows the timing.
+    with_loss = args.with_loss
+
     def step(ev=None):
         theta.copy_(inp.theta0)
         if ev:
@@ -373,13 +381,14 @@ def main():
         for s in range(cfg.steps):
             if ev:
                 ev["g"][s][0].record()
-            tla.ttt_grad_partials(Kp, Vp, theta, H, ws, loss=loss_kind)
+            tla.ttt_grad_partials(Kp, Vp, theta, H, ws, loss=loss_kind, want_loss=with_loss)
             if ev:
                 ev["g"][s][1].record()
+            lrow = loss[s] if with_loss else None
             if opt_kind == "gd":
-                tla.ttt_reduce(ws, n, H, d, m, dt_code, tla.REDUCE_APPLY, theta, cfg.lr, loss[s])
+                tla.ttt_reduce(ws, n, H, d, m, dt_code, tla.REDUCE_APPLY, theta, cfg.lr, lrow)
             else:
-                tla.ttt_reduce(ws, n, H, d, m, dt_code, tla.REDUCE_STORE, gbuf, 0.0, loss[s])
+                tla.ttt_reduce(ws, n, H, d, m, dt_code, tla.REDUCE_STORE, gbuf, 0.0, lrow)
                 tla.ttt_muon_apply(theta, gbuf, cfg.lr, H, d, m, 5)
         if ev:
             ev["w1"].record()
@@ -404,6 +413,10 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
+    if not with_loss:
+        with_loss = True
+        step()
+        torch.cuda.synchronize()
 
     conv_ms = sum(e["c0"].elapsed_time(e["c1"]) for e in events) / args.steps
     write_ms = sum(e["c1"].elapsed_time(e["w1"]) for e in events) / args.steps
@@ -462,6 +475,7 @@ def main():
         "mfma_frac_mlp_contractions": mlp_frac,
         "hbm_GBps": {"conv": conv_bytes / (conv_ms * 1e-3) / 1e9, "read": read_bytes / (read_ms * 1e-3) / 1e9},
         "final_loss_head0": float(loss[-1, 0].item()),
+        "inner_loss_in_timed_step": bool(args.with_loss),
     }
     if args.offload > 0:
         res["offload"] = offload_bench(tla, inp, Vp, cfg, args, loss_kind, opt_kind)

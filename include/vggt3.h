@@ -229,10 +229,15 @@ int vggt3_ttt_grad_partials(const void* K, const void* Vp, const float* theta, i
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* vggt3_ttt_grad_partials for either inner loss (VGGT3_LOSS_*); the reduce is
- * the same for both. */
+ * the same for both. want_loss = 0 skips the loss value: in bf16 the residual
+ * is then never formed and the loss partials hold NaN, so a following
+ * vggt3_ttt_reduce gives a NaN loss_out (the gradient is unchanged, bit for
+ * bit). vggt3_ttt_write and vggt3_ttt_grad do the same when their loss_out is
+ * NULL; vggt3_ttt_grad_partials always computes it. */
 int vggt3_ttt_grad_partials_ex(const void* K, const void* Vp, const float* theta, int64_t n_tokens,
                                int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t loss,
-                               int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+                               int32_t want_loss, int32_t dtype, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 int vggt3_ttt_reduce(const void* workspace, size_t workspace_bytes, int64_t n_tokens, int32_t n_heads,
                      int32_t d_head, int32_t d_hidden, int32_t dtype, int32_t mode, float* dst,

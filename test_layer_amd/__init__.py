@@ -176,17 +176,20 @@ REDUCE_APPLY, REDUCE_STORE, REDUCE_ACCUMULATE = 0, 1, 2
 
 
 def ttt_grad_partials(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, n_heads: int,
-                      workspace: torch.Tensor, d_hidden: Optional[int] = None, loss="mse") -> None:
-    """Per-(head, chunk) gradient and loss partials into `workspace` (Eq. 5 inner sums)."""
+                      workspace: torch.Tensor, d_hidden: Optional[int] = None, loss="mse",
+                      want_loss: bool = True) -> None:
+    """Per-(head, chunk) gradient and loss partials into `workspace` (Eq. 5 inner sums).
+    With want_loss=False the loss partials are not computed (a later reduce's loss is NaN)."""
     _check_dev(K, Vp, theta, workspace)
     d, m = _mlp_dims(theta, K, n_heads, d_hidden)
     lc = _loss_code(loss)
-    if lc == LOSS_MSE:
+    if lc == LOSS_MSE and want_loss:
         _call("vggt3_ttt_grad_partials", _ptr(K), _ptr(Vp), _ptr(theta), K.shape[0], n_heads, d, m,
               _dtype_code(K), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
     else:
         _call("vggt3_ttt_grad_partials_ex", _ptr(K), _ptr(Vp), _ptr(theta), K.shape[0], n_heads, d, m, lc,
-              _dtype_code(K), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+              int(bool(want_loss)), _dtype_code(K), _ptr(workspace), workspace.numel() * workspace.element_size(),
+              _stream())
 
 
 def muon_workspace_bytes(n_heads: int, d_head: int, d_hidden: int) -> int:

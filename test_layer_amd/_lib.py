@@ -42,7 +42,7 @@ SIGNATURES = {
     "vggt3_ttt_grad_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_i64, c_int, c_int, c_int,
                                   c_int, c_int, c_void_p, c_size, c_void_p, c_void_p]),
     "vggt3_ttt_grad_partials_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_int, c_int, c_int, c_int, c_int,
-                                           c_void_p, c_size, c_void_p]),
+                                           c_int, c_void_p, c_size, c_void_p]),
     "vggt3_ttt_muon_apply": (c_int, [c_void_p, c_void_p, c_float, c_int, c_int, c_int, c_int, c_void_p]),
     "vggt3_ttt_stream_stage_bytes": (c_size, [c_i64, c_int, c_int, c_int]),
     "vggt3_ttt_read_workspace_bytes": (c_size, [c_i64, c_int, c_int, c_int, c_int]),

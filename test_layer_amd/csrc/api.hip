@@ -274,20 +274,24 @@ int wide_read(const void* Q, const float* theta, void* O, const MlpArgs& a, void
 
 bool valid_loss(int32_t loss) { return loss == VGGT3_LOSS_MSE || loss == VGGT3_LOSS_DOT; }
 
+// want_loss false: the bf16 kernel skips the loss value (its partials become
+// NaN); the fp32 kernel always computes it.
 hipError_t launch_partials(const void* K, const void* Vp, const float* theta, const MlpArgs& a, void* ws, int P,
-                           int32_t loss, hipStream_t s) {
+                           int32_t loss, bool want_loss, hipStream_t s) {
   const WsLayout l = ws_layout(a, P);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.part);
   float* loss_part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.loss);
   const bool dot = loss == VGGT3_LOSS_DOT;
-  if (a.dt == VGGT3_BF16) return vggt3::launch_grad_partial_bf16(K, Vp, theta, part, loss_part, a.n, a.H, P, dot, s);
+  if (a.dt == VGGT3_BF16)
+    return vggt3::launch_grad_partial_bf16(K, Vp, theta, part, loss_part, a.n, a.H, P, dot, want_loss, s);
   return vggt3::launch_grad_partial_f32(K, Vp, theta, part, loss_part, a.n, a.H, a.d, a.m, P, dot, s);
 }
 
 // Gradient over all tokens into (part, loss_part) then reduce in `mode`.
 int run_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& a, void* ws, int P, int32_t loss,
              vggt3::ReduceMode mode, float* dst, float lr, float* loss_out, hipStream_t s) {
-  int rc = check_hip(launch_partials(K, Vp, theta, a, ws, P, loss, s), "gradient kernel launch");
+  int rc = check_hip(launch_partials(K, Vp, theta, a, ws, P, loss, loss_out != nullptr, s),
+                     "gradient kernel launch");
   if (rc) return rc;
   const WsLayout l = ws_layout(a, P);
   const float* part = reinterpret_cast<const float*>(static_cast<const char*>(ws) + l.part);
@@ -522,8 +526,8 @@ int vggt3_ttt_grad(const void* K, const void* Vp, const float* theta, float* gra
 }
 
 int vggt3_ttt_grad_partials_ex(const void* K, const void* Vp, const float* theta, int64_t n_tokens,
-                               int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t loss, int32_t dtype,
-                               void* workspace, size_t workspace_bytes_, void* stream) {
+                               int32_t n_heads, int32_t d_head, int32_t d_hidden, int32_t loss, int32_t want_loss,
+                               int32_t dtype, void* workspace, size_t workspace_bytes_, void* stream) {
   const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
   int rc = check_mlp(a);
   if (rc) return rc;
@@ -541,15 +545,16 @@ int vggt3_ttt_grad_partials_ex(const void* K, const void* Vp, const float* theta
   if (overlap(workspace, workspace_bytes_, theta, tb) || overlap(workspace, workspace_bytes_, K, xb) ||
       overlap(workspace, workspace_bytes_, Vp, xb))
     return fail(VGGT3_EINVAL, "workspace overlaps another argument");
-  rc = check_hip(launch_partials(K, Vp, theta, a, workspace, P, loss, static_cast<hipStream_t>(stream)),
-                 "gradient kernel launch");
+  rc = check_hip(
+      launch_partials(K, Vp, theta, a, workspace, P, loss, want_loss != 0, static_cast<hipStream_t>(stream)),
+      "gradient kernel launch");
   return rc ? rc : ok();
 }
 
 int vggt3_ttt_grad_partials(const void* K, const void* Vp, const float* theta, int64_t n_tokens, int32_t n_heads,
                             int32_t d_head, int32_t d_hidden, int32_t dtype, void* workspace,
                             size_t workspace_bytes_, void* stream) {
-  return vggt3_ttt_grad_partials_ex(K, Vp, theta, n_tokens, n_heads, d_head, d_hidden, VGGT3_LOSS_MSE, dtype,
+  return vggt3_ttt_grad_partials_ex(K, Vp, theta, n_tokens, n_heads, d_head, d_hidden, VGGT3_LOSS_MSE, 1, dtype,
                                     workspace, workspace_bytes_, stream);
 }
 

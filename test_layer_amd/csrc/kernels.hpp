@@ -34,8 +34,9 @@ hipError_t launch_shortconv_k(const void* V, void* Vp, const float* w, int64_t n
 // Per-(head, chunk) fp32 gradient and loss partials.
 // part: [n_heads][P][3*d*m], loss_part: [n_heads][P]. dot selects the
 // dot-product loss -sum T(k).v' instead of sum (1/d)||T(k) - v'||^2.
+// With loss false the loss partials are written as NaN and the loss work is skipped.
 hipError_t launch_grad_partial_bf16(const void* K, const void* Vp, const float* theta, float* part,
-                                    float* loss_part, int64_t n_tokens, int n_heads, int P, bool dot,
+                                    float* loss_part, int64_t n_tokens, int n_heads, int P, bool dot, bool loss,
                                     hipStream_t stream);
 hipError_t launch_grad_partial_f32(const void* K, const void* Vp, const float* theta, float* part,
                                    float* loss_part, int64_t n_tokens, int n_heads, int d, int m, int P,

@@ -36,6 +36,9 @@
 // same section), dL/dY = -V' does not depend on Y: the Y phase and its two
 // barriers drop out, dH = -V' W_d^T, gW_d += H^T (-V'), and the loss is
 // sum H * dH over the tile (= -sum Y . V').
+// The loss value is a diagnostic: with LOSS false (the caller asked for no
+// loss) the residual R = Y - V' is never formed (the gradient uses Y and -V'
+// as separate operands anyway), and the loss partial is written as NaN.
 // The kernel is sized (about 50 KB of LDS, at most 256 registers per lane, all
 // of them architectural VGPRs, so MFMA results need no copies before VALU use)
 // so that two workgroups share a CU: while one waits at a barrier or on LDS,
@@ -100,7 +103,7 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <bool DOT>
+template <bool DOT, bool LOSS>
 __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
     const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg, const float* __restrict__ theta,
     float* __restrict__ part, float* __restrict__ loss_part, int64_t n_tokens, int n_heads, int P,
@@ -278,15 +281,17 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
       }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const u32x2 vn = ltr(Vc + o_vl + 16 * b);
-        const float r0 = accY[b][0] + bf16_lo(vn[0]);
-        const float r1 = accY[b][1] + bf16_hi(vn[0]);
-        const float r2 = accY[b][2] + bf16_lo(vn[1]);
-        const float r3 = accY[b][3] + bf16_hi(vn[1]);
-        loss = fmaf(r0, r0, loss);
-        loss = fmaf(r1, r1, loss);
-        loss = fmaf(r2, r2, loss);
-        loss = fmaf(r3, r3, loss);
+        if (LOSS) {
+          const u32x2 vn = ltr(Vc + o_vl + 16 * b);
+          const float r0 = accY[b][0] + bf16_lo(vn[0]);
+          const float r1 = accY[b][1] + bf16_hi(vn[0]);
+          const float r2 = accY[b][2] + bf16_lo(vn[1]);
+          const float r3 = accY[b][3] + bf16_hi(vn[1]);
+          loss = fmaf(r0, r0, loss);
+          loss = fmaf(r1, r1, loss);
+          loss = fmaf(r2, r2, loss);
+          loss = fmaf(r3, r3, loss);
+        }
         const uint32_t y01 = pack_bf16x2(accY[b][0], accY[b][1]);
         const uint32_t y23 = pack_bf16x2(accY[b][2], accY[b][3]);
         lu16* yp = Yt + o_yst + 16 * b;
@@ -309,7 +314,7 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
         if (!DOT) accH = mfma32(lop(Yt + o_row + 16 * ks), wdt, accH);
         accH = mfma32(lop(Vc + o_row + 16 * ks), wdt, accH);
       }
-      if (DOT) {
+      if (DOT && LOSS) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) loss = fmaf(Hf[r], accH[r], loss);
       }
@@ -365,6 +370,10 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
       out[DM + e * M + hc] = accWu[b][r] * kScale;
     }
   }
+  if (!LOSS) {
+    if (tid == 0) loss_part[(int64_t)head * P + chunk] = __builtin_nanf("");
+    return;
+  }
   loss = wave_sum(loss);
   if (lane == 0) red[w] = loss;
   __syncthreads();
@@ -375,17 +384,13 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
 }  // namespace
 
 hipError_t launch_grad_partial_bf16(const void* K, const void* Vp, const float* theta, float* part,
-                                    float* loss_part, int64_t n_tokens, int n_heads, int P, bool dot,
+                                    float* loss_part, int64_t n_tokens, int n_heads, int P, bool dot, bool loss,
                                     hipStream_t stream) {
   const int64_t n_blocks = (int64_t)n_heads * P;
-  if (dot)
-    hipLaunchKernelGGL(grad_partial_bf16_kernel<true>, dim3((unsigned)n_blocks), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(Vp), theta, part,
-                       loss_part, n_tokens, n_heads, P, n_blocks);
-  else
-    hipLaunchKernelGGL(grad_partial_bf16_kernel<false>, dim3((unsigned)n_blocks), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(Vp), theta, part,
-                       loss_part, n_tokens, n_heads, P, n_blocks);
+  auto kernel = dot ? (loss ? grad_partial_bf16_kernel<true, true> : grad_partial_bf16_kernel<true, false>)
+                    : (loss ? grad_partial_bf16_kernel<false, true> : grad_partial_bf16_kernel<false, false>);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)n_blocks), dim3(256), 0, stream, static_cast<const uint16_t*>(K),
+                     static_cast<const uint16_t*>(Vp), theta, part, loss_part, n_tokens, n_heads, P, n_blocks);
   return hipGetLastError();
 }
 

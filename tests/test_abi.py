@@ -163,7 +163,7 @@ def test_recipe_entry_points_validate(lib):
     assert write_ex(lr=float("nan")) == tla.EINVAL
     assert lib.vggt3_ttt_grad_ex(FAKE, FAKE2, FAKE3, big, 0, n, H, d, m, 3, tla.BF16, big, ws_need, None,
                                  None) == tla.EINVAL
-    assert lib.vggt3_ttt_grad_partials_ex(FAKE, FAKE2, FAKE3, n, H, d, m, -1, tla.BF16, big, ws_need,
+    assert lib.vggt3_ttt_grad_partials_ex(FAKE, FAKE2, FAKE3, n, H, d, m, -1, 1, tla.BF16, big, ws_need,
                                           None) == tla.EINVAL
     # Muon apply: unsupported shape, bad step count, aliasing, empty
     assert lib.vggt3_ttt_muon_apply(FAKE, FAKE2, 0.1, H, 32, 64, 5, None) == tla.EUNSUPPORTED

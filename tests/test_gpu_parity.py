@@ -216,6 +216,33 @@ def test_write_equals_partials_then_reduce_bitwise():
     np.testing.assert_array_equal(bits(a), bits(c))
 
 
+@pytest.mark.parametrize("loss", ["mse", "dot"])
+def test_loss_value_is_optional_and_leaves_the_gradient_unchanged(loss):
+    """Without a loss output the gradient kernel skips the loss value: the
+    gradient and theta* are the same bits, and a loss asked of such partials is NaN."""
+    cfg = _small_vggt(views=2, steps=2, heads=4)
+    inp = make_inputs(cfg, DEV, with_q=False)
+    Vp = _conv(inp)
+    n, H, d, m = cfg.n_tokens, cfg.n_heads, cfg.d_head, cfg.d_hidden
+    ws = tla.make_workspace(n, H, d, m, tla.BF16)
+    out = {}
+    for want in (True, False):
+        g = torch.empty_like(inp.theta0)
+        lo = torch.zeros(H, device=DEV)
+        tla.ttt_grad_partials(inp.K, Vp, inp.theta0, H, ws, loss=loss, want_loss=want)
+        tla.ttt_reduce(ws, n, H, d, m, tla.BF16, tla.REDUCE_STORE, g, 0.0, lo)
+        out[want] = (g, lo)
+    np.testing.assert_array_equal(bits(out[True][0]), bits(out[False][0]))
+    assert torch.isfinite(out[True][1]).all() and torch.isnan(out[False][1]).all()
+    a = inp.theta0.clone()
+    b = inp.theta0.clone()
+    lw = torch.zeros((cfg.steps, H), device=DEV)
+    tla.ttt_write(inp.K, Vp, a, cfg.lr, cfg.steps, H, loss_out=lw, loss=loss)
+    tla.ttt_write(inp.K, Vp, b, cfg.lr, cfg.steps, H, loss=loss)
+    np.testing.assert_array_equal(bits(a), bits(b))
+    assert torch.isfinite(lw).all()
+
+
 def test_eq5_chunked_gradient_on_gpu():
     """Gradient over all tokens == sum of gradients over two token ranges (accumulate)."""
     cfg = _small_vggt(views=3, heads=4)
