@@ -30,7 +30,7 @@
 // the whole chunk). W_g / W_u operands live in registers, W_d in LDS. Per
 // 32-token tile c the workgroup runs
 //   B0 | G,U(c) ; SwiGLU(c) -> H ; stage K,V'(c+1), load c+2
-//   B1 | Y(c) = H W_d (16x16x32 MFMA tiles over all hidden units) ; loss ; Y -> LDS
+//   B1 | Y(c) = H W_d (16x16x32 MFMA tiles over all hidden units) ; loss ; Y -> LDS [o][t]
 //   B2 | dH(c) = (Y - V') W_d^T ; dG, dU ; gW_d, gW_g, gW_u += tile c
 // With the dot-product loss L = -sum_i T(k_i) . v'_i ("The dot product loss",
 // same section), dL/dY = -V' does not depend on Y: the Y phase and its two
@@ -64,9 +64,10 @@ constexpr int M = 128;     // hidden units
 constexpr int T = 32;      // tokens per tile
 constexpr int DM = D * M;
 constexpr int PER_HEAD = 3 * DM;
-constexpr int TP = VGGT3_WRITE_TP;   // pitch (elements) of [32][64] token tiles: K, -V', Y (all [t][ch])
+constexpr int TP = VGGT3_WRITE_TP;   // pitch (elements) of [32][64] token tiles: K, -V' ([t][ch])
 constexpr int HPT = VGGT3_WRITE_HP;  // pitch of H[hid][t]
 constexpr int WP = VGGT3_WRITE_WP;   // pitch of W_d[hid][o]
+constexpr int YP = 36;               // pitch of Y[o][t]: a lane stores its 4 tokens of one output at once
 constexpr int KV_BUFS = 2;
 constexpr int TSZ = T * TP;          // elements per token tile
 
@@ -78,6 +79,7 @@ constexpr int OFF_H = OFF_Y + TSZ;
 constexpr int OFF_W = OFF_H + M * HPT;
 constexpr int LDS_ELEMS = OFF_W + M * WP;
 static_assert(LDS_ELEMS * 2 <= 80 * 1024, "two workgroups per CU");
+static_assert(64 * YP <= TSZ, "Y tile");
 
 typedef __attribute__((address_space(3))) uint16_t lu16;
 typedef __attribute__((address_space(3))) u32x4 lu32x4;
@@ -178,7 +180,8 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
   const int o_ha = (8 * g4 + jr) * HPT + 16 * tb + 4 * q4;  // Y phase: H^T reads (A operand)
   const int o_wb = (8 * g4 + jr) * WP + 16 * ob + 4 * q4;   // Y phase: W_d reads (B operand)
   const int o_vl = (16 * tb + 4 * g4 + jr) * TP + 16 * ob + 4 * q4;  // Y phase: -V' at the C positions
-  const int o_yst = (16 * tb + 4 * g4) * TP + 16 * ob + i16;         // Y stores (4 rows)
+  const int o_yst = (16 * ob + i16) * YP + 16 * tb + 4 * g4;         // Y stores: 4 tokens of one output
+  const int o_ytr = (8 * hh + jr) * YP + cb + 4 * q4;                // dH phase: Y^T transpose reads
   const int o_wrow = (32 * w + l32) * WP + 8 * hh;          // W_d rows of this wave's units
 
   // Tile staging: thread -> row tid>>3, 8 channels at (tid&7)*8. Loads are
@@ -294,11 +297,7 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
         }
         const uint32_t y01 = pack_bf16x2(accY[b][0], accY[b][1]);
         const uint32_t y23 = pack_bf16x2(accY[b][2], accY[b][3]);
-        lu16* yp = Yt + o_yst + 16 * b;
-        yp[0] = (uint16_t)y01;
-        yp[TP] = (uint16_t)(y01 >> 16);
-        yp[2 * TP] = (uint16_t)y23;
-        yp[3 * TP] = (uint16_t)(y23 >> 16);
+        lst8(Yt + o_yst + 16 * b * YP, u32x2{y01, y23});
       }
     }
     if (!DOT) __syncthreads();  // B2: Y(i) complete
@@ -311,7 +310,10 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 wdt = lop(lds + OFF_W + o_wrow + 16 * ks);  // B[k = o][j = hid]
-        if (!DOT) accH = mfma32(lop(Yt + o_row + 16 * ks), wdt, accH);
+        if (!DOT) {
+          const lu16* yp = Yt + o_ytr + 16 * ks * YP;
+          accH = mfma32(ltr_op(yp, yp + 4 * YP), wdt, accH);
+        }
         accH = mfma32(lop(Vc + o_row + 16 * ks), wdt, accH);
       }
       if (DOT && LOSS) {
@@ -338,9 +340,12 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const lu16* yt = Yt + o_tr + 16 * ks * TP + 32 * nb;
+        const lu16* yt = Yt + (32 * nb + l32) * YP + 16 * ks + 4 * hh;
         const lu16* vt = Vc + o_tr + 16 * ks * TP + 32 * nb;
-        if (!DOT) accWd[nb] = mfma32(Hop[ks], ltr_op(yt, yt + 8 * TP), accWd[nb]);
+        if (!DOT) {
+          const u32x2 y0 = *(const lu32x2*)yt, y1 = *(const lu32x2*)(yt + 8);
+          accWd[nb] = mfma32(Hop[ks], as_bf16x8(u32x4{y0[0], y0[1], y1[0], y1[1]}), accWd[nb]);
+        }
         accWd[nb] = mfma32(Hop[ks], ltr_op(vt, vt + 8 * TP), accWd[nb]);
       }
 #pragma unroll
