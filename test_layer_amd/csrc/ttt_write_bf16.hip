@@ -29,7 +29,7 @@
 // gW_u[:, w-slice], gW_d[w-slice, :] (96 fp32 accumulators per lane, kept for
 // the whole chunk). W_g / W_u operands live in registers, W_d in LDS. Per
 // 32-token tile c the workgroup runs
-//   B0 | G,U(c) ; SwiGLU(c) -> H ; stage K,V'(c+1), load c+2
+//   B0 | G,U(c) ; SwiGLU(c) -> H ; stage K,V'(c+1), load c+3
 //   B1 | Y(c) = H W_d (16x16x32 MFMA tiles over all hidden units) ; loss ; Y -> LDS [o][t]
 //   B2 | dH(c) = (Y - V') W_d^T ; dG, dU ; gW_d, gW_g, gW_u += tile c
 // With the dot-product loss L = -sum_i T(k_i) . v'_i ("The dot product loss",
@@ -191,14 +191,15 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
   const int o_stage = srow * TP + scol;
   const uint16_t* Kh = Kg + (int64_t)head * D + scol;
   const uint16_t* Vh = Vg + (int64_t)head * D + scol;
-  u32x4 kr, vr;
-  auto load_tile = [&](int i) {
+  // Two register sets alternate, so a tile's loads are issued two tiles before
+  // it is staged in LDS.
+  auto load_tile = [&](int i, u32x4& kr, u32x4& vr) {
     int64_t tok = (tile_begin + i) * T + srow;
     tok = tok < n_tokens ? tok : n_tokens - 1;
     kr = ld16(Kh + tok * C);
     vr = ld16(Vh + tok * C);
   };
-  auto store_tile = [&](int i) {
+  auto store_tile = [&](int i, const u32x4& kr, const u32x4& vr) {
     const int buf = i % KV_BUFS;
     const bool ok = (tile_begin + i) * T + srow < n_tokens;
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
@@ -207,14 +208,16 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
           ok ? (vr ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}) : z);
   };
 
+  u32x4 kr0, vr0, kr1, vr1;
   if (nt > 0) {
-    load_tile(0);
-    store_tile(0);
-    if (nt > 1) load_tile(1);
+    load_tile(0, kr0, vr0);
+    store_tile(0, kr0, vr0);
+    load_tile(1, kr1, vr1);
+    load_tile(2, kr0, vr0);
   }
 
   lu16* const Yt = lds + OFF_Y;
-  for (int i = 0; i < nt; ++i) {
+  auto body = [&](int i, u32x4& krs, u32x4& vrs) {
     const lu16* Kc = lds + OFF_K + (i % KV_BUFS) * TSZ;
     const lu16* Vc = lds + OFF_V + (i % KV_BUFS) * TSZ;
     __syncthreads();  // B0: tile i staged; everything of tile i-1 consumed
@@ -261,11 +264,9 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
         lst8(hp + 8, u32x2{hv[2], hv[3]});
       }
     }
-    // Stage tile i+1 (loaded during the previous tile) and start loading i+2.
-    if (i + 1 < nt) {
-      store_tile(i + 1);
-      if (i + 2 < nt) load_tile(i + 2);
-    }
+    // Stage tile i+1 (loaded two tiles ago) and start loading i+3 into its registers.
+    if (i + 1 < nt) store_tile(i + 1, krs, vrs);
+    load_tile(i + 3, krs, vrs);
     if (!DOT) __syncthreads();  // B1: H(i) complete
 
     // Y (tokens 16tb.., outputs 16(ob+b)..) = H W_d over all hidden units;
@@ -356,7 +357,15 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
         accWu[eb] = mfma32(kA, dUop[ks], accWu[eb]);
       }
     }
+  };
+  // Whole pairs in the loop (no conditional body, so the compiler's load waits
+  // stay exact across iterations), an odd last tile after it.
+  int i = 0;
+  for (; i + 1 < nt; i += 2) {
+    body(i, kr1, vr1);
+    body(i + 1, kr0, vr0);
   }
+  if (i < nt) body(i, kr1, vr1);
 
   // Partials in theta layout, times 2/d (mean squared error) or 1 (dot loss).
   constexpr float kScale = DOT ? 1.0f : 2.0f / D;
