@@ -3,9 +3,11 @@
 One step = one pass of the whole layer over the scene, inputs resident in HBM:
   theta <- theta0; V' = ShortConv2D(V); `steps` x (gradient partials over all
   tokens -> fixed-tree reduce + theta -= lr*g); O = read(Q).
-This is exactly the kernel sequence vggt3_ttt_write runs (the write's two
-halves are called through the split C ABI so that the gradient kernel can be
-bracketed by HIP events on the stream it runs on).
+This is exactly the kernel sequence vggt3_ttt_write runs with loss_out = NULL
+(the inner-loss value is computed once, untimed, after the timing; --with-loss
+times it in every step). The write's two halves are called through the split C
+ABI so that the gradient kernel can be bracketed by HIP events on the stream it
+runs on.
 
 Prints ONE JSON line (rank 0) with tokens/s over the scene, the roofline of the
 dominant kernel (the bf16-MFMA gradient pass), per-phase times, and the CPU
@@ -30,9 +32,10 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 SPEC_CLOCK_GHZ = 2.4
 # Shader clock under the gradient kernel, from the committed counter run
-# (profiles/ttt_layer_views1000_counters.md): GPU-active cycles counted at the
-# 2.4 GHz spec (3.411 ms) against the kernel's traced duration (4.215 ms).
-COUNTER_CLOCK_GHZ = round(SPEC_CLOCK_GHZ * 3.411 / 4.215, 2)
+# (profiles/ttt_layer_views1000_counters.md): its GPU-active cycles, converted
+# at the 2.4 GHz spec clock (3.107 ms), against the event-timed launch of the
+# same profiled run (3.877 ms).
+COUNTER_CLOCK_GHZ = round(SPEC_CLOCK_GHZ * 3.107 / 3.877, 2)
 PEAK_HBM_GBS = 8000.0
 METRIC = "TTT-layer tokens/sec (write+read) at 1000 views; % bf16 MFMA peak"
 GRAD_KERNEL = "grad_partial_bf16_kernel"
