@@ -233,25 +233,19 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
     }
 
     // SwiGLU: s = sigmoid(G), A = G s, H = A U, gp = U silu'(G) = U s + H (1 - s).
-    // A and gp are kept as bf16 pairs until the backward step.
-    uint32_t Ap[8], GPp[8];
+    // A and gp stay in fp32 registers until the backward step.
+    float Af[16], GPf[16];
     float Hf[16];
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float a2[2], gp2[2];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const float g = accG[r + k];
-        const float u = accU[r + k];
-        const float s = sigmoid_fast(g);
-        const float a = g * s;
-        const float h = a * u;
-        a2[k] = a;
-        Hf[r + k] = h;
-        gp2[k] = fmaf(-h, s, fmaf(u, s, h));
-      }
-      Ap[r / 2] = pack_bf16x2(a2[0], a2[1]);
-      GPp[r / 2] = pack_bf16x2(gp2[0], gp2[1]);
+    for (int r = 0; r < 16; ++r) {
+      const float g = accG[r];
+      const float u = accU[r];
+      const float s = sigmoid_fast(g);
+      const float a = g * s;
+      const float h = a * u;
+      Af[r] = a;
+      Hf[r] = h;
+      GPf[r] = fmaf(-h, s, fmaf(u, s, h));
     }
     bf16x8 Hop[2];
 #pragma unroll
@@ -323,11 +317,9 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
       }
       float dg[16], du[16];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        du[r] = accH[r] * bf16_lo(Ap[r / 2]);
-        du[r + 1] = accH[r + 1] * bf16_hi(Ap[r / 2]);
-        dg[r] = accH[r] * bf16_lo(GPp[r / 2]);
-        dg[r + 1] = accH[r + 1] * bf16_hi(GPp[r / 2]);
+      for (int r = 0; r < 16; ++r) {
+        du[r] = accH[r] * Af[r];
+        dg[r] = accH[r] * GPf[r];
       }
       dGop[0] = pack8(&dg[0]);
       dGop[1] = pack8(&dg[8]);
