@@ -27,7 +27,9 @@
 // Workgroup = 4 waves; wave w owns hidden units [32w, 32w+32): G, U, H, dH,
 // dG, dU for those units and the matching gradient slices gW_g[:, w-slice],
 // gW_u[:, w-slice], gW_d[w-slice, :] (96 fp32 accumulators per lane, kept for
-// the whole chunk). W_g / W_u operands live in registers, W_d in LDS. Per
+// the whole chunk). W_g / W_u operands live in registers, W_d in LDS twice:
+// [hid][o] for dH, and [o][hid] so that the Y phase reads its operand with
+// plain 16-byte loads (transposing LDS reads cost about twice as much). Per
 // 32-token tile c the workgroup runs
 //   B0 | G,U(c) ; SwiGLU(c) -> H ; stage K,V'(c+1), load c+3
 //   B1 | Y(c) = H W_d (16x16x32 MFMA tiles over all hidden units) ; loss ; Y -> LDS [o][t]
@@ -39,7 +41,7 @@
 // The loss value is a diagnostic: with LOSS false (the caller asked for no
 // loss) the residual R = Y - V' is never formed (the gradient uses Y and -V'
 // as separate operands anyway), and the loss partial is written as NaN.
-// The kernel is sized (about 50 KB of LDS, at most 256 registers per lane, all
+// The kernel is sized (about 67 KB of LDS, at most 256 registers per lane, all
 // of them architectural VGPRs, so MFMA results need no copies before VALU use)
 // so that two workgroups share a CU: while one waits at a barrier or on LDS,
 // the other's MFMA and VALU work fills the SIMDs. All LDS addressing is 32-bit.
@@ -77,7 +79,9 @@ constexpr int OFF_V = OFF_K + KV_BUFS * TSZ;
 constexpr int OFF_Y = OFF_V + KV_BUFS * TSZ;
 constexpr int OFF_H = OFF_Y + TSZ;
 constexpr int OFF_W = OFF_H + M * HPT;
-constexpr int LDS_ELEMS = OFF_W + M * WP;
+constexpr int WTP = M + 8;             // pitch of W_d^T[o][hid]
+constexpr int OFF_WT = OFF_W + M * WP;
+constexpr int LDS_ELEMS = OFF_WT + D * WTP;
 static_assert(LDS_ELEMS * 2 <= 80 * 1024, "two workgroups per CU");
 static_assert(64 * YP <= TSZ, "Y tile");
 
@@ -159,6 +163,14 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
     *(__attribute__((address_space(3))) uint32_t*)(lds + OFF_W + hid * WP + o) =
         pack_bf16x2(Wd[hid * D + o], Wd[hid * D + o + 1]);
   }
+  // and transposed, [o][hid], for the Y phase's B operand.
+  if (!DOT) {
+    for (int idx = tid; idx < M * D / 2; idx += 256) {
+      const int o = (2 * idx) / M, hid = (2 * idx) % M;
+      *(__attribute__((address_space(3))) uint32_t*)(lds + OFF_WT + o * WTP + hid) =
+          pack_bf16x2(Wd[hid * D + o], Wd[(hid + 1) * D + o]);
+    }
+  }
 
   f32x16 accWd[2], accWg[2], accWu[2];
 #pragma unroll
@@ -178,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
   const int o_tr = (4 * hh + jr) * TP + cb + 4 * q4;        // transpose reads over token rows
   const int o_hst = (32 * w + l32) * HPT + 4 * hh;          // H stores
   const int o_ha = (8 * g4 + jr) * HPT + 16 * tb + 4 * q4;  // Y phase: H^T reads (A operand)
-  const int o_wb = (8 * g4 + jr) * WP + 16 * ob + 4 * q4;   // Y phase: W_d reads (B operand)
+  const int o_wtb = (16 * ob + i16) * WTP + 8 * g4;         // Y phase: W_d^T reads (B operand)
   const int o_vl = (16 * tb + 4 * g4 + jr) * TP + 16 * ob + 4 * q4;  // Y phase: -V' at the C positions
   const int o_yst = (16 * ob + i16) * YP + 16 * tb + 4 * g4;         // Y stores: 4 tokens of one output
   const int o_ytr = (8 * hh + jr) * YP + cb + 4 * q4;                // dH phase: Y^T transpose reads
@@ -272,10 +284,8 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
         const lu16* hp = lds + OFF_H + o_ha + 32 * ks * HPT;
         const bf16x8 ha = ltr_op(hp, hp + 4 * HPT);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const lu16* wp = lds + OFF_W + o_wb + 32 * ks * WP + 16 * b;
-          accY[b] = mfma16(ha, ltr_op(wp, wp + 4 * WP), accY[b]);
-        }
+        for (int b = 0; b < 2; ++b)
+          accY[b] = mfma16(ha, lop(lds + OFF_WT + o_wtb + 16 * b * WTP + 32 * ks), accY[b]);
       }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
