@@ -59,7 +59,7 @@ extern "C" {
 enum {
   VGGT3_OK = 0,
   VGGT3_EINVAL = -1,       /* null/misaligned/aliased pointer, negative size, bad lr/steps */
-  VGGT3_EUNSUPPORTED = -2, /* shape or dtype this build has no kernel for */
+  VGGT3_EUNSUPPORTED = -2, /* shape or dtype the library has no kernel for */
   VGGT3_EWORKSPACE = -3,   /* workspace missing or smaller than vggt3_ttt_workspace_bytes */
   VGGT3_EHIP = -4          /* the HIP runtime refused a launch */
 };

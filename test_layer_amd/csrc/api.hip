@@ -49,7 +49,7 @@ size_t elem_size(int32_t dt) { return dt == VGGT3_BF16 ? 2 : 4; }
 // The pages' full-width MLP: one 1024 -> 4096 -> 1024 SwiGLU (one "head").
 bool is_wide(int32_t d, int32_t m) { return d == vggt3::wide::kD && m == vggt3::wide::kM; }
 
-// Shapes with a kernel in this build.
+// Shapes the library has kernels for.
 bool supported_mlp(int32_t dt, int32_t d, int32_t m) {
   if (dt == VGGT3_BF16) return (d == 64 && m == 128) || is_wide(d, m);
   if (dt == VGGT3_F32) return (d == 16 && m == 32) || (d == 64 && m == 128);
