@@ -393,6 +393,8 @@ def main():
             else:
                 tla.ttt_reduce(ws, n, H, d, m, dt_code, tla.REDUCE_STORE, gbuf, 0.0, lrow)
                 tla.ttt_muon_apply(theta, gbuf, cfg.lr, H, d, m, 5)
+            if ev:
+                ev["u"][s].record()
         if ev:
             ev["w1"].record()
         tla.ttt_read(inp.Q, theta, H, out=O)
@@ -406,7 +408,8 @@ def main():
         step()
     torch.cuda.synchronize()
     events = [{"c0": mk(), "c1": mk(), "w1": mk(), "r1": mk(),
-               "g": [(mk(), mk()) for _ in range(cfg.steps)]} for _ in range(args.steps)]
+               "g": [(mk(), mk()) for _ in range(cfg.steps)], "u": [mk() for _ in range(cfg.steps)]}
+              for _ in range(args.steps)]
     start, end = mk(), mk()
     torch.cuda.synchronize()
     start.record()
@@ -426,6 +429,10 @@ def main():
     read_ms = sum(e["w1"].elapsed_time(e["r1"]) for e in events) / args.steps
     grad_ms = [a.elapsed_time(b) for e in events for (a, b) in e["g"]]
     grad_avg_ms = sum(grad_ms) / len(grad_ms)
+    # The update after each gradient pass: the fixed-tree reduce of the chunk
+    # partials plus theta -= lr g (and, for Muon, the Newton-Schulz update).
+    upd_ms = [e["g"][s][1].elapsed_time(e["u"][s]) for e in events for s in range(cfg.steps)]
+    update_avg_ms = sum(upd_ms) / len(upd_ms)
 
     fw, fr = flops_per_token(cfg, loss_kind)
     grad_flops = fw * n  # per launch of the gradient kernel
@@ -434,6 +441,11 @@ def main():
     esz = 2 if cfg.dtype == "bf16" else 4
     conv_bytes = 2 * n * H * d * esz * (2 if args.conv_variant == "kv3" else 1)
     read_bytes = 2 * nq * H * d * esz
+    # Gradient-descent update: the partials (the workspace less its theta-sized
+    # gradient buffer and at most 4 KB of loss partials) read once, theta read
+    # and written.
+    theta_bytes = theta.numel() * theta.element_size()
+    update_bytes = (ws.numel() * ws.element_size() - theta_bytes) + 2 * theta_bytes
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -474,9 +486,10 @@ def main():
             "avg_launch_ms": grad_avg_ms,
             "flops_per_launch": grad_flops,
         },
-        "phases_ms": {"conv": conv_ms, "write": write_ms, "read": read_ms},
+        "phases_ms": {"conv": conv_ms, "write": write_ms, "read": read_ms, "update_each": update_avg_ms},
         "mfma_frac_mlp_contractions": mlp_frac,
-        "hbm_GBps": {"conv": conv_bytes / (conv_ms * 1e-3) / 1e9, "read": read_bytes / (read_ms * 1e-3) / 1e9},
+        "hbm_GBps": {"conv": conv_bytes / (conv_ms * 1e-3) / 1e9, "read": read_bytes / (read_ms * 1e-3) / 1e9,
+                     "update": (update_bytes / (update_avg_ms * 1e-3) / 1e9) if opt_kind == "gd" else None},
         "final_loss_head0": float(loss[-1, 0].item()),
         "inner_loss_in_timed_step": bool(args.with_loss),
     }
