@@ -488,6 +488,10 @@ def main():
         },
         "phases_ms": {"conv": conv_ms, "write": write_ms, "read": read_ms, "update_each": update_avg_ms},
         "mfma_frac_mlp_contractions": mlp_frac,
+        # Scene tokens through conv + write alone, and the read's own query rate
+        # (the query-mode read of unseen views reads fewer tokens than the scene).
+        "scene_tokens_per_s_without_read": n / ((conv_ms + write_ms) * 1e-3),
+        "read_tokens_per_s": nq / (read_ms * 1e-3),
         "hbm_GBps": {"conv": conv_bytes / (conv_ms * 1e-3) / 1e9, "read": read_bytes / (read_ms * 1e-3) / 1e9,
                      "update": (update_bytes / (update_avg_ms * 1e-3) / 1e9) if opt_kind == "gd" else None},
         "final_loss_head0": float(loss[-1, 0].item()),
