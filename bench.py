@@ -33,9 +33,9 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 SPEC_CLOCK_GHZ = 2.4
 # Shader clock under the gradient kernel, from the committed counter run
 # (profiles/ttt_layer_views1000_counters.md): its GPU-active cycles, converted
-# at the 2.4 GHz spec clock (2.905 ms), against the event-timed launch of the
-# same profiled run (3.806 ms).
-COUNTER_CLOCK_GHZ = round(SPEC_CLOCK_GHZ * 2.905 / 3.806, 2)
+# at the 2.4 GHz spec clock (2.815 ms), against the event-timed launch of the
+# same profiled run (3.762 ms).
+COUNTER_CLOCK_GHZ = round(SPEC_CLOCK_GHZ * 2.815 / 3.762, 2)
 PEAK_HBM_GBS = 8000.0
 METRIC = "TTT-layer tokens/sec (write+read) at 1000 views; % bf16 MFMA peak"
 GRAD_KERNEL = "grad_partial_bf16_kernel"

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(512, 2) void read_bf16_kernel(const uint16_t* __res
   const int chunk = (int)(blk % P);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so tile offsets stay scalar
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int64_t C = (int64_t)n_heads * D;
@@ -70,22 +70,28 @@ __global__ __launch_bounds__(512, 2) void read_bf16_kernel(const uint16_t* __res
   const int64_t tile_end = n_tiles * (chunk + 1) / P;
 
   // Each wave walks tiles tile_begin + w, + NW, ...; the next tile's queries
-  // are loaded while the current one computes.
-  // Loads are unconditional (rows past the end read the last token and are
-  // never stored), so the compiler's load-counter waits stay exact.
+  // are loaded while the current one computes. Q and O are accessed through
+  // buffer descriptors built per tile from 64-bit scalar arithmetic, based at
+  // the tile's first token and this head, with a range that ends at the
+  // tensor's end: rows at or past n_tokens read as zeros and their stores are
+  // dropped, so loads and stores are unconditional and the lane offsets fixed.
+  const int lane_off = (l32 * (int)C + 32 * hh) * 2;
+  auto tile_res = [&](const uint16_t* base, int64_t tile) {
+    const int64_t t0 = tile * RT;
+    const int64_t range = (n_tokens - t0) * C * 2 - (int64_t)head * D * 2;
+    const int nrec = (int)(range > 0x7fffffffLL ? 0x7fffffffLL : (range > 0 ? range : 0));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + t0 * C + (int64_t)head * D), (short)0, nrec, 0x00020000);
+  };
   auto load_q = [&](int64_t tile, u32x4 (&dst)[4]) {
-    int64_t t = tile * RT + l32;
-    t = t < n_tokens ? t : n_tokens - 1;
-    const uint16_t* src = Q + t * C + (int64_t)head * D + 32 * hh;
+    const __amdgpu_buffer_rsrc_t r = tile_res(Q, tile);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) dst[ks] = ld16(src + 8 * ks);
+    for (int ks = 0; ks < 4; ++ks)
+      dst[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off + 16 * ks, 0, 0));
   };
   // Two query register sets alternate (no loop-carried copies, so the load
   // waits stay exact): tile k computes from one set while tile k+1 loads into
   // the other.
   auto compute_tile = [&](int64_t tile, const u32x4 (&qr)[4]) {
-    const int64_t t = tile * RT + l32;
-    const bool valid = t < n_tokens;
     bf16x8 q[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) q[ks] = as_bf16x8(qr[ks]);
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(512, 2) void read_bf16_kernel(const uint16_t* __res
     // half hh. Exchanging the q-odd quads of the low half with the q-even
     // quads of the high half (v_permlane32_swap) gives every lane 8
     // consecutive outputs, stored as one 16-byte write.
-    uint16_t* dst = O + t * C + (int64_t)head * D;
+    const __amdgpu_buffer_rsrc_t ores = tile_res(O, tile);
 #pragma unroll
     for (int ot = 0; ot < 2; ++ot) {
 #pragma unroll
@@ -133,8 +139,8 @@ __global__ __launch_bounds__(512, 2) void read_bf16_kernel(const uint16_t* __res
         const uint32_t x0 = pack_bf16x2(a[8 * p + 4], a[8 * p + 5]), x1 = pack_bf16x2(a[8 * p + 6], a[8 * p + 7]);
         const auto s0 = __builtin_amdgcn_permlane32_swap(y0, x0, false, false);
         const auto s1 = __builtin_amdgcn_permlane32_swap(y1, x1, false, false);
-        if (valid)
-          *reinterpret_cast<u32x4*>(dst + 32 * ot + 16 * p + 8 * hh) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{s0[0], s1[0], s0[1], s1[1]}, ores,
+                                               (l32 * (int)C + 32 * ot + 16 * p + 8 * hh) * 2, 0, 0);
       }
     }
   };

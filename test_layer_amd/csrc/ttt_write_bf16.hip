@@ -196,28 +196,30 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
   const int o_ytr = (8 * hh + jr) * YP + cb + 4 * q4;                // dH phase: Y^T transpose reads
   const int o_wrow = (32 * w + l32) * WP + 8 * hh;          // W_d rows of this wave's units
 
-  // Tile staging: thread -> row tid>>3, 8 channels at (tid&7)*8. Loads are
-  // unconditional (rows past the end re-read the last token and are zeroed),
-  // which keeps the compiler's load-counter waits exact.
+  // Tile staging: thread -> row tid>>3, 8 channels at (tid&7)*8. K and V'
+  // are read through buffer descriptors built per tile from 64-bit scalar
+  // arithmetic: based at the tile's first token and this head, with a range
+  // that ends at the tensor's end. The lane offset is fixed; rows at or past
+  // n_tokens lie beyond the range and read as zeros, which also keeps the loads
+  // unconditional, so the compiler's load-counter waits stay exact.
   const int srow = tid >> 3, scol = (tid & 7) * 8;
   const int o_stage = srow * TP + scol;
-  const uint16_t* Kh = Kg + (int64_t)head * D + scol;
-  const uint16_t* Vh = Vg + (int64_t)head * D + scol;
-  // Two register sets alternate, so a tile's loads are issued two tiles before
-  // it is staged in LDS.
+  const int lane_off = (srow * (int)C + scol) * 2;
   auto load_tile = [&](int i, u32x4& kr, u32x4& vr) {
-    int64_t tok = (tile_begin + i) * T + srow;
-    tok = tok < n_tokens ? tok : n_tokens - 1;
-    kr = ld16(Kh + tok * C);
-    vr = ld16(Vh + tok * C);
+    const int64_t t0 = (tile_begin + i) * T;
+    const int64_t off = t0 * C + (int64_t)head * D;
+    const int64_t range = (n_tokens - t0) * C * 2 - (int64_t)head * D * 2;  // bytes to the tensor's end
+    const int nrec = (int)(range > 0x7fffffffLL ? 0x7fffffffLL : (range > 0 ? range : 0));
+    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + off), (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + off), (short)0, nrec, 0x00020000);
+    kr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, lane_off, 0, 0));
+    vr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, lane_off, 0, 0));
   };
+  // V' is staged negated (rows past the end become -0, which adds nothing).
   auto store_tile = [&](int i, const u32x4& kr, const u32x4& vr) {
     const int buf = i % KV_BUFS;
-    const bool ok = (tile_begin + i) * T + srow < n_tokens;
-    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-    lst16(lds + OFF_K + buf * TSZ + o_stage, ok ? kr : z);
-    lst16(lds + OFF_V + buf * TSZ + o_stage,
-          ok ? (vr ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}) : z);
+    lst16(lds + OFF_K + buf * TSZ + o_stage, kr);
+    lst16(lds + OFF_V + buf * TSZ + o_stage, vr ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u});
   };
 
   u32x4 kr0, vr0, kr1, vr1;
