@@ -26,6 +26,8 @@ constexpr int PER_HEAD = 3 * DM;
 // ---------------------------------------------------------------------------
 constexpr int RT = 32;  // tokens per wave iteration
 constexpr int NW = 8;   // waves per workgroup
+// Two workgroups per CU (four waves per SIMD) need at most 128 VGPRs per lane;
+// the kernel compiles to 128 (check num_vgpr in the assembly after changes).
 
 __global__ __launch_bounds__(512, 2) void read_bf16_kernel(const uint16_t* __restrict__ Q,
                                                            const float* __restrict__ theta,
