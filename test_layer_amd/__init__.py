@@ -63,6 +63,32 @@ def _check_dev(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _check_tokens(name: str, t: torch.Tensor) -> None:
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D [tokens, channels] tensor, got shape {tuple(t.shape)}")
+    _dtype_code(t)
+
+
+def _check_same(name: str, t: Optional[torch.Tensor], ref: torch.Tensor, ref_name: str) -> None:
+    if t is None:
+        return
+    if t.shape != ref.shape or t.dtype != ref.dtype:
+        raise ValueError(f"{name} {tuple(t.shape)} {t.dtype} does not match {ref_name} {tuple(ref.shape)} {ref.dtype}")
+
+
+def _check_f32(name: str, t: Optional[torch.Tensor], numel: int, at_least: bool = False) -> None:
+    if t is None:
+        return
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32, got {t.dtype}")
+    if (t.numel() < numel) if at_least else (t.numel() != numel):
+        raise ValueError(f"{name} has {t.numel()} elements, {'at least ' if at_least else ''}{numel} expected")
+
+
+def _check_theta(theta: torch.Tensor, n_heads: int, d: int, m: int) -> None:
+    _check_f32("theta", theta, n_heads * 3 * d * m)
+
+
 def _call(name: str, *args) -> int:
     rc = getattr(lib(), name)(*args)
     if rc != OK:
@@ -74,11 +100,17 @@ def shortconv(V: torch.Tensor, w: torch.Tensor, n_views: int, grid_h: int, grid_
               out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """V' = depthwise k x k ShortConv2D of each view's patch grid (k = w.shape[-1],
     3 or 5); special tokens copied."""
+    _check_tokens("V", V)
+    if w.dtype != torch.float32 or w.dim() != 3 or w.shape[1] != w.shape[2]:
+        raise TypeError("conv weights are float32 [C, k, k]")
+    if w.shape[0] != V.shape[1]:
+        raise ValueError(f"conv weights have {w.shape[0]} channels, V has {V.shape[1]}")
+    if V.shape[0] != n_views * (n_special + grid_h * grid_w):
+        raise ValueError(f"V has {V.shape[0]} tokens, {n_views} views x ({n_special} + {grid_h}x{grid_w}) expected")
+    _check_same("out", out, V, "V")
     if out is None:
         out = torch.empty_like(V)
     _check_dev(V, w, out)
-    if w.dtype != torch.float32 or w.dim() != 3 or w.shape[1] != w.shape[2]:
-        raise TypeError("conv weights are float32 [C, k, k]")
     k = int(w.shape[-1])
     if k == 3:
         _call("vggt3_shortconv", _ptr(V), _ptr(out), _ptr(w), n_views, grid_h, grid_w, n_special, V.shape[1],
@@ -133,8 +165,12 @@ def ttt_write(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, lr: float,
     loss: "mse" (default) or "dot"; optimizer: "gd" (default) or "muon" with
     `ns_steps` Newton-Schulz iterations.
     """
-    _check_dev(K, Vp, theta, workspace, loss_out)
+    _check_tokens("K", K)
+    _check_same("Vp", Vp, K, "K")
     d, m = _mlp_dims(theta, K, n_heads, d_hidden)
+    _check_theta(theta, n_heads, d, m)
+    _check_f32("loss_out", loss_out, max(int(steps), 0) * n_heads, at_least=True)
+    _check_dev(K, Vp, theta, workspace, loss_out)
     dt = _dtype_code(K)
     if workspace is None:
         workspace = make_workspace(K.shape[0], n_heads, d, m, dt, K.device)
@@ -154,10 +190,15 @@ def ttt_grad(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, n_heads: in
              workspace: Optional[torch.Tensor] = None, loss_out: Optional[torch.Tensor] = None,
              loss="mse") -> torch.Tensor:
     """Gradient of the inner loss at theta (Eq. 5 split: accumulate=True adds to grad)."""
+    _check_tokens("K", K)
+    _check_same("Vp", Vp, K, "K")
+    d, m = _mlp_dims(theta, K, n_heads, d_hidden)
+    _check_theta(theta, n_heads, d, m)
+    _check_f32("grad", grad, n_heads * 3 * d * m)
+    _check_f32("loss_out", loss_out, n_heads, at_least=True)
     if grad is None:
         grad = torch.empty_like(theta)
     _check_dev(K, Vp, theta, grad, workspace, loss_out)
-    d, m = _mlp_dims(theta, K, n_heads, d_hidden)
     dt = _dtype_code(K)
     if workspace is None:
         workspace = make_workspace(K.shape[0], n_heads, d, m, dt, K.device)
@@ -180,8 +221,11 @@ def ttt_grad_partials(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, n_
                       want_loss: bool = True) -> None:
     """Per-(head, chunk) gradient and loss partials into `workspace` (Eq. 5 inner sums).
     With want_loss=False the loss partials are not computed (a later reduce's loss is NaN)."""
-    _check_dev(K, Vp, theta, workspace)
+    _check_tokens("K", K)
+    _check_same("Vp", Vp, K, "K")
     d, m = _mlp_dims(theta, K, n_heads, d_hidden)
+    _check_theta(theta, n_heads, d, m)
+    _check_dev(K, Vp, theta, workspace)
     lc = _loss_code(loss)
     if lc == LOSS_MSE and want_loss:
         _call("vggt3_ttt_grad_partials", _ptr(K), _ptr(Vp), _ptr(theta), K.shape[0], n_heads, d, m,
@@ -200,6 +244,8 @@ def ttt_muon_apply(theta: torch.Tensor, grad: torch.Tensor, lr: float, n_heads: 
                    d_hidden: int, ns_steps: int = 5, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """theta -= lr * NS(grad) per head and weight matrix (Muon update), in place
     (the full-width 1024 -> 4096 MLP takes a workspace)."""
+    _check_theta(theta, n_heads, d_head, d_hidden)
+    _check_f32("grad", grad, n_heads * 3 * d_head * d_hidden)
     _check_dev(theta, grad, workspace)
     need = muon_workspace_bytes(n_heads, d_head, d_hidden)
     if need == 0 and workspace is None:
@@ -216,6 +262,8 @@ def ttt_muon_apply(theta: torch.Tensor, grad: torch.Tensor, lr: float, n_heads: 
 def ttt_reduce(workspace: torch.Tensor, n_tokens: int, n_heads: int, d_head: int, d_hidden: int, dtype_code: int,
                mode: int, dst: torch.Tensor, lr: float = 0.0, loss_out: Optional[torch.Tensor] = None) -> None:
     """Fixed-tree sum of the partials, then apply to theta / store / accumulate into dst."""
+    _check_f32("dst", dst, n_heads * 3 * d_head * d_hidden)
+    _check_f32("loss_out", loss_out, n_heads, at_least=True)
     _check_dev(workspace, dst, loss_out)
     _call("vggt3_ttt_reduce", _ptr(workspace), workspace.numel() * workspace.element_size(), n_tokens, n_heads,
           d_head, d_hidden, dtype_code, mode, _ptr(dst), float(lr), _ptr(loss_out), _stream())
@@ -223,6 +271,8 @@ def ttt_reduce(workspace: torch.Tensor, n_tokens: int, n_heads: int, d_head: int
 
 def ttt_apply(theta: torch.Tensor, grad: torch.Tensor, lr: float, n_heads: int, d_head: int,
               d_hidden: int) -> torch.Tensor:
+    _check_theta(theta, n_heads, d_head, d_hidden)
+    _check_f32("grad", grad, n_heads * 3 * d_head * d_hidden)
     _check_dev(theta, grad)
     _call("vggt3_ttt_apply", _ptr(theta), _ptr(grad), float(lr), n_heads, d_head, d_hidden, _stream())
     return theta
@@ -235,10 +285,13 @@ def read_workspace_bytes(n_tokens: int, n_heads: int, d_head: int, d_hidden: int
 def ttt_read(Q: torch.Tensor, theta: torch.Tensor, n_heads: int, d_hidden: Optional[int] = None,
              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """O = T_theta(Q) per head (the full-width 1024 -> 4096 MLP reads through a workspace)."""
+    _check_tokens("Q", Q)
+    _check_same("out", out, Q, "Q")
+    d, m = _mlp_dims(theta, Q, n_heads, d_hidden)
+    _check_theta(theta, n_heads, d, m)
     if out is None:
         out = torch.empty_like(Q)
     _check_dev(Q, theta, out, workspace)
-    d, m = _mlp_dims(theta, Q, n_heads, d_hidden)
     dt = _dtype_code(Q)
     need = read_workspace_bytes(Q.shape[0], n_heads, d, m, dt)
     if workspace is None and need > 0:
@@ -307,9 +360,13 @@ def ttt_write_streamed(K_host: torch.Tensor, Vp_host: torch.Tensor, theta: torch
     The copies run on `copy_stream` (default: a side stream of this device)
     while the kernels run on the current stream; the host tensors must stay
     untouched until the current stream has been synchronised."""
+    _check_tokens("K_host", K_host)
+    _check_same("Vp_host", Vp_host, K_host, "K_host")
+    d, m = _mlp_dims(theta, K_host, n_heads, d_hidden)
+    _check_theta(theta, n_heads, d, m)
+    _check_f32("loss_out", loss_out, max(int(steps), 0) * n_heads, at_least=True)
     _check_host(K_host, Vp_host)
     _check_dev(theta, stage, workspace, loss_out)
-    d, m = _mlp_dims(theta, K_host, n_heads, d_hidden)
     dt = _dtype_code(K_host)
     n = K_host.shape[0]
     ct = max(1, min(int(chunk_tokens), n))
@@ -335,11 +392,14 @@ def ttt_read_streamed(Q_host: torch.Tensor, theta: torch.Tensor, n_heads: int, c
     """O = T_theta(Q) for host-resident Q, written to a host tensor (query mode
     over a frozen theta), streamed in chunks of `chunk_tokens`. `out` defaults
     to a new pinned tensor; read it after synchronising the current stream."""
+    _check_tokens("Q_host", Q_host)
+    _check_same("out", out, Q_host, "Q_host")
+    d, m = _mlp_dims(theta, Q_host, n_heads, d_hidden)
+    _check_theta(theta, n_heads, d, m)
     if out is None:
         out = torch.empty(Q_host.shape, dtype=Q_host.dtype, pin_memory=True)
     _check_host(Q_host, out)
     _check_dev(theta, stage)
-    d, m = _mlp_dims(theta, Q_host, n_heads, d_hidden)
     dt = _dtype_code(Q_host)
     n = Q_host.shape[0]
     ct = max(1, min(int(chunk_tokens), n))

@@ -56,7 +56,8 @@ bool supported_mlp(int32_t dt, int32_t d, int32_t m) {
   return false;
 }
 
-int tile_tokens(int32_t dt) { return dt == VGGT3_BF16 ? 64 : 16; }
+// Token tile of the gradient kernel of each dtype (the unit of the Eq. 5 chunking).
+int tile_tokens(int32_t dt) { return dt == VGGT3_BF16 ? vggt3::kGradTileBf16 : vggt3::kGradTileF32; }
 
 struct MlpArgs {
   int64_t n;

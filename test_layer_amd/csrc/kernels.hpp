@@ -22,6 +22,10 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t n) {
 // fixed pairwise tree, so results do not depend on the GPU's CU count.
 constexpr int kMaxChunks = 64;
 int ttt_num_chunks(int64_t n_tokens, int n_heads, int tile_tokens);
+// Tokens per tile of the gradient kernels: the unit a chunk is cut in. The
+// kernels assert that they tile by these, and the chunk count is taken from them.
+constexpr int kGradTileBf16 = 32;
+constexpr int kGradTileF32 = 16;
 
 // Widest patch-grid row the ShortConv2D kernel stages in LDS.
 int shortconv_max_grid_w();

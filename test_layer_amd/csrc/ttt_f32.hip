@@ -17,6 +17,7 @@ namespace {
 template <int D, int M>
 struct F32Cfg {
   static constexpr int TT = 16;  // tokens per tile
+  static_assert(TT == kGradTileF32, "the chunking cuts tokens in units of this tile");
   static constexpr int DM = D * M;
   static constexpr int PER_HEAD = 3 * DM;
   static constexpr int NACC = PER_HEAD / 256;

@@ -64,6 +64,7 @@ namespace {
 constexpr int D = 64;      // inputs / outputs of T per head
 constexpr int M = 128;     // hidden units
 constexpr int T = 32;      // tokens per tile
+static_assert(T == kGradTileBf16, "the chunking cuts tokens in units of this tile");
 constexpr int DM = D * M;
 constexpr int PER_HEAD = 3 * DM;
 constexpr int TP = VGGT3_WRITE_TP;   // pitch (elements) of [32][64] token tiles: K, -V' ([t][ch])

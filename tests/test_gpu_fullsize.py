@@ -80,16 +80,73 @@ def test_views24_full_layer():
     assert e.max() <= TOL_BF16, e
 
 
-@pytest.mark.parametrize("name", ["views1000", "views2000"])
-def test_full_scene_sampled(name):
-    """1000 / 2000 views, 2 steps, exactly as timed. Checked: conv on sampled views
-    (the first and the last, whose byte offsets exceed 2^31), the gradient of one
-    sampled head over all tokens at theta0 and at theta1, that each step applies
-    theta - lr*g, and the read on a 1% token sample (for 2000 views: the 50 unseen
-    query views, frozen theta*)."""
+def test_views100_full_layer():
+    """100 views (137,400 tokens), 16 heads, 2 steps, everything checked in full
+    against the oracle: the conv bit for bit, each step's gradient (the GPU's at
+    its own theta_s against the oracle's at the oracle's theta_s), each step's
+    loss, theta*, delta-theta, and the read of all 137,400 queries with theta*.
+    The fused write equals the gradient + apply sequence bit for bit."""
+    cfg = CONFIGS["views100"]
+    n = cfg.n_tokens
+    print(f"[views100] n={n}", flush=True)
+    inp = make_inputs(cfg, DEV)
+    Vp = tla.shortconv(inp.V, inp.conv_w, cfg.n_views, cfg.grid_h, cfg.grid_w, cfg.n_special)
+    ws = tla.make_workspace(n, cfg.n_heads, cfg.d_head, cfg.d_hidden, tla.BF16)
+    theta = inp.theta0.clone()
+    grads = []
+    for _ in range(cfg.steps):
+        g = tla.ttt_grad(inp.K, Vp, theta, cfg.n_heads, workspace=ws)
+        grads.append(g)
+        tla.ttt_apply(theta, g, cfg.lr, cfg.n_heads, cfg.d_head, cfg.d_hidden)
+    theta_w = inp.theta0.clone()
+    loss = torch.empty((cfg.steps, cfg.n_heads), device=DEV)
+    tla.ttt_write(inp.K, Vp, theta_w, cfg.lr, cfg.steps, cfg.n_heads, workspace=ws, loss_out=loss)
+    O = tla.ttt_read(inp.Q, theta_w, cfg.n_heads)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(theta_w), bits(theta))
+    print("  gpu done", flush=True)
+
+    Vp_ref = oracle.shortconv(to64(inp.V).astype(np.float32), inp.conv_w.cpu().numpy(), cfg.n_views, cfg.grid_h,
+                              cfg.grid_w, cfg.n_special, out="bf16")
+    np.testing.assert_array_equal(bits(Vp), f32_to_bits(Vp_ref, True))
+    print("  conv bit-exact", flush=True)
+    th0 = inp.theta0.cpu().numpy().astype(np.float64)
+    th_ref, L_ref, g_ref = oracle.ttt_write(to64(inp.K), Vp_ref.astype(np.float64), th0, cfg.n_heads, cfg.d_head,
+                                            cfg.d_hidden, cfg.lr, cfg.steps, chunk=1 << 17)
+    for s in range(cfg.steps):
+        e = rel_err_per_head(grads[s].cpu().numpy().astype(np.float64), g_ref[s], cfg.n_heads, axis_cols=False)
+        le = np.abs(loss[s].cpu().numpy() - L_ref[s]) / L_ref[s]
+        print(f"  step {s + 1}: gradient rel err max {e.max():.3e}, loss {le.max():.3e}", flush=True)
+        assert e.max() <= TOL_BF16, e
+        assert le.max() <= TOL_BF16, le
+    th = theta.cpu().numpy().astype(np.float64)
+    dth = rel_err_per_head(th - th0, th_ref - th0, cfg.n_heads, axis_cols=False)
+    print(f"  delta-theta rel err max {dth.max():.3e}", flush=True)
+    assert dth.max() <= TOL_BF16, dth
+    assert rel_err_per_head(th, th_ref, cfg.n_heads, axis_cols=False).max() <= TOL_BF16
+    O_ref = oracle.ttt_read(to64(inp.Q), th_ref, cfg.n_heads, cfg.d_head, cfg.d_hidden)
+    e = rel_err_per_head(to64(O), O_ref, cfg.n_heads)
+    print(f"  read rel err max {e.max():.3e}", flush=True)
+    assert e.max() <= TOL_BF16, e
+
+
+@pytest.mark.parametrize("name,h", [("views1000", 5), ("views2000", 15)])
+def test_full_scene_sampled(name, h):
+    """1000 / 2000 views, 2 steps, exactly as timed (whole scene in HBM, one call
+    per phase). Checked against the oracle:
+      * the conv on sampled views (the first and the last, whose byte offsets
+        exceed 2^31) and on all tokens of head h;
+      * a 2-step oracle write of head h over all n tokens (heads are
+        independent): the GPU's gradient at theta0 and at its theta1, each
+        step's loss, theta* and delta-theta of that head;
+      * the read with theta* of head h's columns for every query (2000 views:
+        the 50 unseen query views, frozen theta*);
+      * the read with theta0 of all heads on a 1% token sample.
+    Also: each step applies theta - lr*g in fp32, and the fused write gives the
+    same theta* bit for bit. h = 15 is the last head, whose columns end the row."""
     cfg = CONFIGS[name]
     n = cfg.n_tokens
-    print(f"[{name}] n={n}", flush=True)
+    print(f"[{name}] n={n} head {h}", flush=True)
     inp = make_inputs(cfg, DEV)
     Vp = tla.shortconv(inp.V, inp.conv_w, cfg.n_views, cfg.grid_h, cfg.grid_w, cfg.n_special)
     ws = tla.make_workspace(n, cfg.n_heads, cfg.d_head, cfg.d_hidden, tla.BF16)
@@ -103,37 +160,55 @@ def test_full_scene_sampled(name):
         thetas.append(theta.clone())
     # the fused write gives the same theta* bit for bit
     theta_w = inp.theta0.clone()
-    tla.ttt_write(inp.K, Vp, theta_w, cfg.lr, cfg.steps, cfg.n_heads, workspace=ws)
+    loss = torch.empty((cfg.steps, cfg.n_heads), device=DEV)
+    tla.ttt_write(inp.K, Vp, theta_w, cfg.lr, cfg.steps, cfg.n_heads, workspace=ws, loss_out=loss)
     O = tla.ttt_read(inp.Q, theta_w, cfg.n_heads)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits(theta_w), bits(theta))
     print("  gpu done", flush=True)
+    # each step is theta - lr * g in fp32
+    for s in range(cfg.steps):
+        exp = thetas[s] - cfg.lr * grads[s]
+        np.testing.assert_allclose(thetas[s + 1].cpu().numpy(), exp.cpu().numpy(), rtol=0, atol=1e-7)
 
     # conv on sampled views incl. the last one
     views = sorted({0, 1, cfg.n_views // 2, cfg.n_views - 1})
     _check_conv_views(cfg, inp, Vp, views)
     print("  conv ok", flush=True)
 
-    # gradient of one head over all tokens, at theta0 (oracle conv of all views for that head)
-    h = 5
+    # head h over all tokens: oracle conv of that head's channels, then a 2-step oracle write
     cols = slice(h * cfg.d_head, (h + 1) * cfg.d_head)
     Kh = to64(inp.K[:, cols])
     Vh = inp.V[:, cols].to(torch.float32).cpu().numpy()
     w_h = inp.conv_w[cols].cpu().numpy()
     Vp_h = oracle.shortconv(Vh, w_h, cfg.n_views, cfg.grid_h, cfg.grid_w, cfg.n_special, out="bf16")
     np.testing.assert_array_equal(bits(Vp[:, cols].contiguous()), f32_to_bits(Vp_h, True))
-    th0 = inp.theta0.cpu().numpy()
-    g_ref, _ = oracle.ttt_grad(Kh, Vp_h.astype(np.float64), th0[h:h + 1], 1, cfg.d_head, cfg.d_hidden,
-                               chunk=1 << 17)
-    e0 = rel_err(grads[0][h].cpu().numpy().astype(np.float64), g_ref[0])
-    print(f"  grad head {h} at theta0: rel err {e0:.3e}", flush=True)
-    assert e0 <= TOL_BF16
-    # each step is theta - lr * g in fp32
+    del Vh
+    th0 = inp.theta0.cpu().numpy().astype(np.float64)
+    th_ref, L_ref, g_ref = oracle.ttt_write(Kh, Vp_h.astype(np.float64), th0[h:h + 1], 1, cfg.d_head,
+                                            cfg.d_hidden, cfg.lr, cfg.steps, chunk=1 << 17)
+    del Kh, Vp_h
     for s in range(cfg.steps):
-        exp = thetas[s] - cfg.lr * grads[s]
-        np.testing.assert_allclose(thetas[s + 1].cpu().numpy(), exp.cpu().numpy(), rtol=0, atol=1e-7)
+        e = rel_err(grads[s][h].cpu().numpy().astype(np.float64), g_ref[s][0])
+        le = abs(float(loss[s, h]) - L_ref[s, 0]) / L_ref[s, 0]
+        print(f"  head {h} step {s + 1}: gradient rel err {e:.3e}, loss {le:.3e}", flush=True)
+        assert e <= TOL_BF16
+        assert le <= TOL_BF16
+    th_h = theta_w[h].cpu().numpy().astype(np.float64)
+    dth = rel_err(th_h - th0[h], th_ref[0] - th0[h])
+    print(f"  head {h} delta-theta rel err {dth:.3e} (|dtheta|/|theta0| = "
+          f"{np.abs(th_ref[0] - th0[h]).max() / np.abs(th0[h]).max():.2e})", flush=True)
+    assert dth <= TOL_BF16
+    assert rel_err(th_h, th_ref[0]) <= TOL_BF16
 
-    # read on a token sample, with theta0 and head-local oracle theta1 for head h
+    # read with theta*: head h's columns for every query
+    Oh_ref = oracle.ttt_read(to64(inp.Q[:, cols]), th_ref, 1, cfg.d_head, cfg.d_hidden)
+    eo = rel_err(to64(O[:, cols]), Oh_ref)
+    print(f"  head {h} read with theta* over {O.shape[0]} queries: rel err {eo:.3e}", flush=True)
+    assert eo <= TOL_BF16
+    del Oh_ref
+
+    # read with theta0, all heads, on a 1% token sample
     nq = inp.Q.shape[0]
     rows = _sample(nq, 0.01, 3, must=(0, nq - 1))
     rt = torch.from_numpy(rows).to(DEV)
@@ -152,9 +227,9 @@ def test_views1000_pages_recipe_sampled():
     """1000 views with the pages' recipe (dot-product loss, Muon), as
     `bench.py --recipe dot_muon` times it. Checked: the dot-loss gradient of one
     sampled head over all tokens at theta0, and that head's first Muon step
-    against the oracle's (bar 2e-2 times the oracle-measured Newton-Schulz
-    error gain, see tests/test_gpu_recipe.py); the fused write equals the
-    gradient + Muon-apply sequence bit for bit."""
+    against the oracle's at the plain 2e-2 bar (the oracle-measured
+    Newton-Schulz error gain is printed as a diagnostic); the fused write
+    equals the gradient + Muon-apply sequence bit for bit."""
     from tests.test_gpu_recipe import _ns_gain
     cfg = CONFIGS["views1000"]
     n = cfg.n_tokens
@@ -187,4 +262,4 @@ def test_views1000_pages_recipe_sampled():
     d1 = rel_err(theta1[h].cpu().numpy().astype(np.float64) - th0[0], th1_ref[0] - th0[0])
     print(f"  dot grad head {h}: rel err {e0:.3e}; Muon step: {d1:.3e} (NS gain {kappa:.2f})", flush=True)
     assert e0 <= TOL_BF16
-    assert d1 <= TOL_BF16 * kappa
+    assert d1 <= TOL_BF16

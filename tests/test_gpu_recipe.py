@@ -6,12 +6,12 @@ The oracle side is oracle.ttt_grad / ttt_write with loss="dot", opt="muon"
 Bar (per head, normwise max error):
   * dot-loss gradient and loss: 2e-2 (bf16 compute), 1e-4 (fp32 compute);
   * the Muon map theta - lr NS(g) on a given fp32 gradient: 1e-4 (fp32 kernel);
-  * a whole Muon write: the fp32 path at 1e-4; the bf16 path at 2e-2 times the
-    Newton-Schulz error gain kappa. NS is not a contraction near the origin:
-    it raises small singular values steeply, so a relative gradient error e
-    turns into an output error of up to kappa*e. kappa is measured on the
-    oracle's own gradient, by finite perturbation of the oracle's NS (no GPU
-    value enters that measurement).
+  * a whole Muon write: the fp32 path at 1e-4, the bf16 path at 2e-2.
+    NS is not a contraction near the origin: it raises small singular values
+    steeply, so a relative gradient error e can turn into an output error of
+    up to kappa*e. kappa is measured on the oracle's own gradient, by finite
+    perturbation of the oracle's NS (no GPU value enters that measurement),
+    and printed beside the error as a diagnostic; it does not widen the bar.
 """
 from __future__ import annotations
 
@@ -221,13 +221,13 @@ def test_write_dot_muon_bf16_parity():
     th_ref, L_ref, g_ref = oracle.ttt_write(K64, Vp_ref, th0, cfg.n_heads, cfg.d_head, cfg.d_hidden, cfg.lr,
                                             cfg.steps, loss="dot", opt="muon")
     kappa = max(_ns_gain(g_ref[s], cfg.n_heads, cfg.d_head, cfg.d_hidden) for s in range(cfg.steps))
-    tol = TOL_BF16 * kappa
+    tol = TOL_BF16
     th = theta.cpu().numpy().astype(np.float64)
     dth = rel_err_per_head(th - th0, th_ref - th0, cfg.n_heads, axis_cols=False)
     lerr = _dot_loss_err(loss.cpu().numpy()[0], L_ref[0], K64, Vp_ref, th0, cfg.n_heads, cfg.d_head, cfg.d_hidden)
     O_ref = oracle.ttt_read(to64(inp.Q), th_ref, cfg.n_heads, cfg.d_head, cfg.d_hidden)
     oerr = rel_err_per_head(to64(O), O_ref, cfg.n_heads)
-    print(f"  NS gain {kappa:.2f} -> tol {tol:.3e}; delta-theta {dth.max():.3e}, loss {lerr.max():.3e}, "
+    print(f"  NS gain {kappa:.2f} (diagnostic), tol {tol:.3e}; delta-theta {dth.max():.3e}, loss {lerr.max():.3e}, "
           f"read {oerr.max():.3e}", flush=True)
     assert dth.max() <= tol, dth
     assert lerr.max() <= tol, lerr

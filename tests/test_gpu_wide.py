@@ -183,8 +183,8 @@ def _ns_gain(g, trials=2, eps=1e-3, seed=0):
 
 def test_wide_write_dot_muon_parity():
     """The pages' recipe at the pages' width: dot-product loss, Muon with 5
-    Newton-Schulz steps, 2 steps. Bar 2e-2 times the NS error gain, as for the
-    per-head Muon write."""
+    Newton-Schulz steps, 2 steps. Bar 2e-2, as for the per-head Muon write;
+    the oracle-measured NS error gain is printed as a diagnostic."""
     cfg = _cfg(steps=2)
     print("[wide] dot + muon write", flush=True)
     inp, Vp = _scene(cfg)
@@ -196,9 +196,9 @@ def test_wide_write_dot_muon_parity():
     K64, Vp_ref = to64(inp.K), _oracle_vp(inp)
     th_ref, L_ref, grads = oracle.ttt_write(K64, Vp_ref, th0, 1, D, M, cfg.lr, 2, loss="dot", opt="muon")
     kappa = _ns_gain(grads[0])
-    tol = TOL * kappa
+    tol = TOL
     ok, worst = dtheta_ok(theta.cpu().numpy().astype(np.float64), th_ref, th0, 1, tol, 2)
-    print(f"  NS gain {kappa:.2f}, dtheta worst/allowance {worst:.3f} (tol {tol:.3g})", flush=True)
+    print(f"  NS gain {kappa:.2f} (diagnostic), dtheta worst/allowance {worst:.3f} (tol {tol:.3g})", flush=True)
     assert ok, worst
 
 
