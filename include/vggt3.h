@@ -27,7 +27,9 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
  *     aligned (the streamed entry points at the end take HOST token tensors,
  *     as they say). The library allocates no device memory and keeps no state
- *     between calls apart from a per-thread last-error string.
+ *     between calls apart from a per-thread last-error string and the fixed
+ *     scratch array of vggt3_ttt_write_noalloc (one per GPU, held until the
+ *     process ends).
  *   - Token tensors (K, V, V', Q, O) are row-major [n_tokens][C] with
  *     C = n_heads * d_head; head h owns columns h*d_head .. h*d_head+d_head-1.
  *     Within a scene, tokens are grouped by view, and each view is
@@ -179,6 +181,29 @@ int vggt3_ttt_write_ex(const void* K, const void* Vp, float* theta, int64_t n_to
                        int32_t d_head, int32_t d_hidden, float lr, int32_t steps, int32_t loss,
                        int32_t optimizer, int32_t ns_steps, int32_t dtype, void* workspace,
                        size_t workspace_bytes, float* loss_out, void* stream);
+
+/*
+ * vggt3_ttt_write_ex without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. It calls no allocating routine; its
+ * workspace is a fixed array of VGGT3_NOALLOC_SCRATCH_BYTES in the library's
+ * device memory, one per GPU (resident from the library's first use on that
+ * GPU until the process ends), located once per device.
+ *   - Limit: calls whose workspace (vggt3_ttt_workspace_bytes) exceeds
+ *     VGGT3_NOALLOC_SCRATCH_BYTES return VGGT3_EWORKSPACE; the 64 MiB hold any
+ *     token count at up to 16 heads of the (64, 128) MLP. The full-width
+ *     (1024, 4096) MLP returns VGGT3_EUNSUPPORTED.
+ *   - All calls on one GPU share that GPU's array: calls that may run at the
+ *     same time on one GPU (other host threads, other streams) race and must
+ *     be serialised by the caller. Nothing in the array needs clearing: each
+ *     call writes every byte it reads.
+ * Results are bitwise those of vggt3_ttt_write_ex with its own workspace.
+ */
+#define VGGT3_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int vggt3_ttt_write_noalloc(const void* K, const void* Vp, float* theta, int64_t n_tokens, int32_t n_heads,
+                            int32_t d_head, int32_t d_hidden, float lr, int32_t steps, int32_t loss,
+                            int32_t optimizer, int32_t ns_steps, int32_t dtype, float* loss_out,
+                            void* stream);
 
 /*
  * Gradient of the inner loss at theta over n_tokens tokens ([GRAPH] Eq. 5: the

@@ -185,6 +185,26 @@ def ttt_write(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, lr: float,
     return theta
 
 
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+
+
+def ttt_write_noalloc(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, lr: float, steps: int, n_heads: int,
+                      d_hidden: Optional[int] = None, loss_out: Optional[torch.Tensor] = None, loss="mse",
+                      optimizer="gd", ns_steps: int = 5) -> torch.Tensor:
+    """ttt_write through vggt3_ttt_write_noalloc: no workspace, nothing allocated
+    (the library's fixed per-GPU scratch array serves as the workspace)."""
+    _check_tokens("K", K)
+    _check_same("Vp", Vp, K, "K")
+    d, m = _mlp_dims(theta, K, n_heads, d_hidden)
+    _check_theta(theta, n_heads, d, m)
+    _check_f32("loss_out", loss_out, max(int(steps), 0) * n_heads, at_least=True)
+    _check_dev(K, Vp, theta, loss_out)
+    _call("vggt3_ttt_write_noalloc", _ptr(K), _ptr(Vp), _ptr(theta), K.shape[0], n_heads, d, m, float(lr),
+          int(steps), _loss_code(loss), _opt_code(optimizer), int(ns_steps), _dtype_code(K), _ptr(loss_out),
+          _stream())
+    return theta
+
+
 def ttt_grad(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, n_heads: int,
              grad: Optional[torch.Tensor] = None, accumulate: bool = False, d_hidden: Optional[int] = None,
              workspace: Optional[torch.Tensor] = None, loss_out: Optional[torch.Tensor] = None,

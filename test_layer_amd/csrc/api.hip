@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/vggt3.h"
@@ -333,6 +334,55 @@ size_t stage_slot_bytes(int64_t chunk_tokens, int32_t C, int32_t dt) {
   return round256((size_t)chunk_tokens * C * elem_size(dt));
 }
 
+// Arguments of a write call other than its workspace (host-side only).
+int check_write_args(const MlpArgs& a, const void* K, const void* Vp, const float* theta, float lr, int32_t steps,
+                     int32_t loss, int32_t optimizer, int32_t ns_steps, const float* loss_out) {
+  int rc = check_mlp(a);
+  if (rc) return rc;
+  if (!valid_loss(loss)) return fail(VGGT3_EINVAL, "unknown loss %d", loss);
+  if (optimizer != VGGT3_OPT_GD && optimizer != VGGT3_OPT_MUON)
+    return fail(VGGT3_EINVAL, "unknown optimizer %d", optimizer);
+  if (optimizer == VGGT3_OPT_MUON && (ns_steps < 0 || ns_steps > VGGT3_MAX_NS_STEPS))
+    return fail(VGGT3_EINVAL, "ns_steps = %d outside [0, %d]", ns_steps, VGGT3_MAX_NS_STEPS);
+  if (!std::isfinite(lr)) return fail(VGGT3_EINVAL, "lr is not finite");
+  if (steps < 1) return fail(VGGT3_EINVAL, "steps = %d < 1", steps);
+  if (theta == nullptr) return fail(VGGT3_EINVAL, "theta is NULL");
+  if (!aligned16(theta) || (loss_out && !aligned16(loss_out)))
+    return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  if (a.n > 0) {
+    if (K == nullptr || Vp == nullptr) return fail(VGGT3_EINVAL, "K or V' is NULL");
+    if (!aligned16(K) || !aligned16(Vp)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  }
+  return VGGT3_OK;
+}
+
+// Fixed scratch of vggt3_ttt_write_noalloc: one copy per GPU, in the code
+// object's device memory, alive until the process ends. In host code the
+// name below is only a stand-in; the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[VGGT3_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on its first use).
+int scratch_address(void** out) {
+  int dev = 0;
+  int rc = check_hip(hipGetDevice(&dev), "hipGetDevice");
+  if (rc) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(VGGT3_EUNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    rc = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (rc) return rc;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VGGT3_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -396,22 +446,8 @@ int vggt3_ttt_write_ex(const void* K, const void* Vp, float* theta, int64_t n_to
                        int32_t ns_steps, int32_t dtype, void* workspace, size_t workspace_bytes_, float* loss_out,
                        void* stream) {
   const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
-  int rc = check_mlp(a);
+  int rc = check_write_args(a, K, Vp, theta, lr, steps, loss, optimizer, ns_steps, loss_out);
   if (rc) return rc;
-  if (!valid_loss(loss)) return fail(VGGT3_EINVAL, "unknown loss %d", loss);
-  if (optimizer != VGGT3_OPT_GD && optimizer != VGGT3_OPT_MUON)
-    return fail(VGGT3_EINVAL, "unknown optimizer %d", optimizer);
-  if (optimizer == VGGT3_OPT_MUON && (ns_steps < 0 || ns_steps > VGGT3_MAX_NS_STEPS))
-    return fail(VGGT3_EINVAL, "ns_steps = %d outside [0, %d]", ns_steps, VGGT3_MAX_NS_STEPS);
-  if (!std::isfinite(lr)) return fail(VGGT3_EINVAL, "lr is not finite");
-  if (steps < 1) return fail(VGGT3_EINVAL, "steps = %d < 1", steps);
-  if (theta == nullptr) return fail(VGGT3_EINVAL, "theta is NULL");
-  if (!aligned16(theta) || (loss_out && !aligned16(loss_out)))
-    return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
-  if (a.n > 0) {
-    if (K == nullptr || Vp == nullptr) return fail(VGGT3_EINVAL, "K or V' is NULL");
-    if (!aligned16(K) || !aligned16(Vp)) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
-  }
   int P = 1;
   rc = check_workspace(a, workspace, workspace_bytes_, &P);
   if (rc) return rc;
@@ -472,6 +508,31 @@ int vggt3_ttt_write(const void* K, const void* Vp, float* theta, int64_t n_token
                     size_t workspace_bytes_, float* loss_out, void* stream) {
   return vggt3_ttt_write_ex(K, Vp, theta, n_tokens, n_heads, d_head, d_hidden, lr, steps, VGGT3_LOSS_MSE,
                             VGGT3_OPT_GD, 0, dtype, workspace, workspace_bytes_, loss_out, stream);
+}
+
+int vggt3_ttt_write_noalloc(const void* K, const void* Vp, float* theta, int64_t n_tokens, int32_t n_heads,
+                            int32_t d_head, int32_t d_hidden, float lr, int32_t steps, int32_t loss,
+                            int32_t optimizer, int32_t ns_steps, int32_t dtype, float* loss_out, void* stream) {
+  const MlpArgs a{n_tokens, n_heads, d_head, d_hidden, dtype};
+  int rc = check_write_args(a, K, Vp, theta, lr, steps, loss, optimizer, ns_steps, loss_out);
+  if (rc) return rc;
+  if (is_wide(a.d, a.m))
+    return fail(VGGT3_EUNSUPPORTED, "the %d -> %d -> %d MLP needs a workspace of GBs; use vggt3_ttt_write_ex",
+                a.d, a.m, a.d);
+  // Every byte of the workspace this call uses is written by its own kernels
+  // before it is read (chunk partials, loss partials, reduced gradient), so
+  // the scratch needs no clearing between calls.
+  const size_t need = workspace_bytes(a, nullptr);
+  if (need > (size_t)VGGT3_NOALLOC_SCRATCH_BYTES)
+    return fail(VGGT3_EWORKSPACE, "needs %zu bytes of scratch, more than the fixed %zu (fewer heads fit)", need,
+                (size_t)VGGT3_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+  }
+  return vggt3_ttt_write_ex(K, Vp, theta, n_tokens, n_heads, d_head, d_hidden, lr, steps, loss, optimizer,
+                            ns_steps, dtype, ws, need, loss_out, stream);
 }
 
 int vggt3_ttt_grad_ex(const void* K, const void* Vp, const float* theta, float* grad, int32_t accumulate,
