@@ -129,6 +129,44 @@ def test_wide_gradient_eq5_split_and_determinism():
     assert e.max() <= 1e-5, e
 
 
+def test_wide_two_chunk_scene_against_oracle():
+    """102 views = 140,148 tokens: one full 131,072-token chunk of the GEMM
+    sequence and a ragged second one, so the in-HBM write accumulates two
+    chunks. Against the oracle: the gradient at theta0 and both steps' losses,
+    theta* and delta-theta of a 2-step write, and the read with theta* on rows
+    on both sides of the chunk boundary and at the tail."""
+    cfg = _cfg(views=102, steps=2)
+    n = cfg.n_tokens
+    assert 131_072 < n < 2 * 131_072
+    print(f"[wide] two-chunk scene n={n}", flush=True)
+    inp, Vp = _scene(cfg, with_q=True)
+    L0 = torch.empty(1, device=DEV)
+    g0 = tla.ttt_grad(inp.K, Vp, inp.theta0, 1, loss_out=L0)
+    theta = inp.theta0.clone()
+    L = torch.empty((2, 1), device=DEV)
+    tla.ttt_write(inp.K, Vp, theta, cfg.lr, 2, 1, loss_out=L)
+    rows = np.unique(np.concatenate([np.linspace(0, n - 1, 120).astype(np.int64), 131_072 + np.arange(-6, 6),
+                                     np.arange(n - 20, n)]))
+    O = tla.ttt_read(inp.Q, theta, 1)
+    torch.cuda.synchronize()
+    print("  gpu done", flush=True)
+    th0 = inp.theta0.cpu().numpy().astype(np.float64)
+    th_ref, L_ref, g_ref = oracle.ttt_write(to64(inp.K), _oracle_vp(inp), th0, 1, D, M, cfg.lr, 2)
+    e = _per_matrix_err(to64(g0), g_ref[0])
+    le = [abs(float(L[s, 0]) - L_ref[s, 0]) / abs(L_ref[s, 0]) for s in range(2)]
+    print(f"  gradient at theta0 per-matrix rel err {e}; loss rel err {le}", flush=True)
+    assert e.max() <= TOL, e
+    assert max(le) <= TOL
+    assert abs(L0.item() - L_ref[0, 0]) <= TOL * abs(L_ref[0, 0])
+    ok, worst = dtheta_ok(theta.cpu().numpy().astype(np.float64), th_ref, th0, 1, TOL, 2)
+    print(f"  delta-theta worst/allowance {worst:.3f}", flush=True)
+    assert ok, worst
+    O_ref = oracle.ttt_read(to64(inp.Q[torch.from_numpy(rows).to(DEV)]), th_ref, 1, D, M)
+    er = rel_err(to64(O[torch.from_numpy(rows).to(DEV)]), O_ref)
+    print(f"  read with theta* on {rows.size} rows: rel err {er:.3e}", flush=True)
+    assert er <= TOL, er
+
+
 def test_wide_views1000_chunked_gradient_and_sampled_read():
     """The 1000-view scene (1,374,000 tokens: ten full 131,072-token chunks and a
     ragged one). The gradient cannot be checked against the oracle at this
