@@ -194,6 +194,42 @@ def offload_bench(tla, inp, Vp, cfg, args, loss_kind, opt_kind):
     }
 
 
+def conv_fused_bench(tla, inp, cfg, args, loss_kind, opt_kind, ws, O):
+    """Time the layer step with the ShortConv2D fused into the write
+    (vggt3_ttt_write_conv) in its two forms, beside the split step:
+    "all": every gradient pass forms V' itself (V' never in memory);
+    "first": the first pass forms V' and writes it, the second reads it."""
+    import torch
+    n, H = cfg.n_tokens, cfg.n_heads
+    out = {}
+    for mode in ("all", "first"):
+        theta = inp.theta0.clone()
+        Vo = torch.empty_like(inp.V) if mode == "first" else None
+
+        def write():
+            theta.copy_(inp.theta0)
+            tla.ttt_write_conv(inp.K, inp.V, inp.conv_w, cfg.n_views, cfg.grid_h, cfg.grid_w, cfg.n_special, theta,
+                               cfg.lr, cfg.steps, H, Vp_out=Vo, workspace=ws, loss=loss_kind, optimizer=opt_kind)
+
+        for _ in range(args.warmup):
+            write()
+            tla.ttt_read(inp.Q, theta, H, out=O)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ev[3 * i].record()
+            write()
+            ev[3 * i + 1].record()
+            tla.ttt_read(inp.Q, theta, H, out=O)
+            ev[3 * i + 2].record()
+        torch.cuda.synchronize()
+        step_ms = sum(ev[3 * i].elapsed_time(ev[3 * i + 2]) for i in range(args.steps)) / args.steps
+        write_ms = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(args.steps)) / args.steps
+        out[mode] = {"ms_per_step": step_ms, "tokens_per_s": n / (step_ms * 1e-3), "conv_and_write_ms": write_ms}
+        del Vo
+    return out
+
+
 def wide_bench(args, loss_kind, opt_kind, recipe_desc):
     """The pages' full-width fast-weight MLP (one 1024 -> 4096 -> 1024 SwiGLU
     over the whole token) on the same scene: conv, `steps` write steps through
@@ -299,6 +335,11 @@ def wide_bench(args, loss_kind, opt_kind, recipe_desc):
     }
     if args.offload > 0:
         res["offload"] = offload_bench(tla, inp, Vp, cfg, args, loss_kind, opt_kind)
+    if args.conv_fused:
+        if cfg.dtype != "bf16" or args.conv_variant != "v3":
+            raise SystemExit("--conv-fused takes the bf16 workloads with the 3x3 conv on V")
+        res["conv_fused"] = conv_fused_bench(tla, inp, cfg, args, loss_kind, opt_kind, ws, O)
+        res["conv_fused"]["split_conv_and_write_ms"] = conv_ms + write_ms
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, cfg, loss=loss_kind, opt=opt_kind)
     print(json.dumps(res), flush=True)
@@ -324,6 +365,9 @@ def main():
     ap.add_argument("--offload", type=int, default=0, metavar="CHUNK",
                     help="also time the offloaded step (K, V', Q in pinned host memory, streamed through the GPU in "
                          "CHUNK-token chunks; O streamed back) and report it under 'offload' (never as value)")
+    ap.add_argument("--conv-fused", action="store_true",
+                    help="also time the step with the ShortConv2D fused into the write (vggt3_ttt_write_conv), "
+                         "V' formed in every pass or only in the first, and report it under 'conv_fused'")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()

@@ -206,6 +206,38 @@ int vggt3_ttt_write_noalloc(const void* K, const void* Vp, float* theta, int64_t
                             void* stream);
 
 /*
+ * Write with the ShortConv2D fused into every gradient pass ([GRAPH] "Non-
+ * Linear Spatial Mixing via ShortConv2D" and Appendix A feed the write with
+ * V' = conv(V); here V' is formed tile by tile inside the gradient kernel, so
+ * it need not exist in device memory).
+ *
+ *   K, V      [n_views*(n_special+grid_h*grid_w)][C], bf16; read only. V is
+ *             the unconvolved value tensor.
+ *   conv_w    float32 [C][3][3], as w of vggt3_shortconv.
+ *   Vp_out    NULL, or [n_tokens][C] bf16: then the first step also writes
+ *             V' there (bitwise the output of vggt3_shortconv) and later steps
+ *             read it instead of recomputing it. Must not overlap any other
+ *             argument.
+ * theta, lr, steps, loss, optimizer, ns_steps, workspace (sized by
+ * vggt3_ttt_workspace_bytes(n_tokens, n_heads, 64, 128, VGGT3_BF16)) and
+ * loss_out as in vggt3_ttt_write_ex. Results are bitwise those of
+ * vggt3_shortconv followed by vggt3_ttt_write_ex.
+ * Supported: bf16, (d_head, d_hidden) = (64, 128), grid_w <= 47 (a tile's
+ * 3x3 window must fit the kernel's 128-row ring), n_special + grid_h*grid_w
+ * <= 65504; other shapes return VGGT3_EUNSUPPORTED. n_views == 0 leaves theta
+ * unchanged (losses written as 0).
+ * Cost: the conv's vector work adds about as much time to each gradient pass
+ * as the separate conv pass takes, so with V' in memory the split path
+ * (vggt3_shortconv + vggt3_ttt_write_ex) is as fast or faster; this form
+ * saves the n_tokens*C*2 bytes of V'.
+ */
+int vggt3_ttt_write_conv(const void* K, const void* V, const float* conv_w, int64_t n_views, int32_t grid_h,
+                         int32_t grid_w, int32_t n_special, float* theta, int32_t n_heads, int32_t d_head,
+                         int32_t d_hidden, float lr, int32_t steps, int32_t loss, int32_t optimizer,
+                         int32_t ns_steps, void* Vp_out, void* workspace, size_t workspace_bytes,
+                         float* loss_out, void* stream);
+
+/*
  * Gradient of the inner loss at theta over n_tokens tokens ([GRAPH] Eq. 5: the
  * full gradient is the sum of per-minibatch gradients, so chunks of a scene
  * can be fed in any number of calls with accumulate = 1).

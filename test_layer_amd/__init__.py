@@ -205,6 +205,36 @@ def ttt_write_noalloc(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, lr
     return theta
 
 
+def ttt_write_conv(K: torch.Tensor, V: torch.Tensor, conv_w: torch.Tensor, n_views: int, grid_h: int, grid_w: int,
+                   n_special: int, theta: torch.Tensor, lr: float, steps: int, n_heads: int,
+                   Vp_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   loss_out: Optional[torch.Tensor] = None, loss="mse", optimizer="gd",
+                   ns_steps: int = 5) -> torch.Tensor:
+    """ShortConv2D + write with the 3x3 conv formed inside each gradient pass
+    (vggt3_ttt_write_conv): V' never has to exist in device memory. With
+    Vp_out, the first step also writes V' there and later steps read it.
+    bf16, (d_head, d_hidden) = (64, 128); theta is updated in place."""
+    _check_tokens("K", K)
+    _check_same("V", V, K, "K")
+    if conv_w.dtype != torch.float32 or tuple(conv_w.shape) != (K.shape[1], 3, 3):
+        raise ValueError(f"conv_w must be float32 [{K.shape[1]}, 3, 3]")
+    if K.shape[0] != n_views * (n_special + grid_h * grid_w):
+        raise ValueError(f"K has {K.shape[0]} tokens, {n_views} views x ({n_special} + {grid_h}x{grid_w}) expected")
+    _check_same("Vp_out", Vp_out, K, "K")
+    d, m = _mlp_dims(theta, K, n_heads, None)
+    _check_theta(theta, n_heads, d, m)
+    _check_f32("loss_out", loss_out, max(int(steps), 0) * n_heads, at_least=True)
+    _check_dev(K, V, conv_w, theta, Vp_out, workspace, loss_out)
+    dt = _dtype_code(K)
+    if workspace is None:
+        workspace = make_workspace(K.shape[0], n_heads, d, m, dt, K.device)
+    nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("vggt3_ttt_write_conv", _ptr(K), _ptr(V), _ptr(conv_w), n_views, grid_h, grid_w, n_special, _ptr(theta),
+          n_heads, d, m, float(lr), int(steps), _loss_code(loss), _opt_code(optimizer), int(ns_steps),
+          _ptr(Vp_out), _ptr(workspace), nb, _ptr(loss_out), _stream())
+    return theta
+
+
 def ttt_grad(K: torch.Tensor, Vp: torch.Tensor, theta: torch.Tensor, n_heads: int,
              grad: Optional[torch.Tensor] = None, accumulate: bool = False, d_hidden: Optional[int] = None,
              workspace: Optional[torch.Tensor] = None, loss_out: Optional[torch.Tensor] = None,

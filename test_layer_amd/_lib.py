@@ -31,6 +31,9 @@ SIGNATURES = {
                                 c_int, c_void_p, c_size, c_void_p, c_void_p]),
     "vggt3_ttt_write_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_int, c_int, c_int, c_float, c_int,
                                         c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
+    "vggt3_ttt_write_conv": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_int, c_int, c_int, c_void_p, c_int,
+                                     c_int, c_int, c_float, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_size,
+                                     c_void_p, c_void_p]),
     "vggt3_ttt_grad": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_i64, c_int, c_int, c_int,
                                c_int, c_void_p, c_size, c_void_p, c_void_p]),
     "vggt3_ttt_grad_partials": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_int, c_int, c_int, c_int,

@@ -289,18 +289,27 @@ hipError_t launch_partials(const void* K, const void* Vp, const float* theta, co
   return vggt3::launch_grad_partial_f32(K, Vp, theta, part, loss_part, a.n, a.H, a.d, a.m, P, dot, s);
 }
 
-// Gradient over all tokens into (part, loss_part) then reduce in `mode`.
-int run_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& a, void* ws, int P, int32_t loss,
-             vggt3::ReduceMode mode, float* dst, float lr, float* loss_out, hipStream_t s) {
-  int rc = check_hip(launch_partials(K, Vp, theta, a, ws, P, loss, loss_out != nullptr, s),
-                     "gradient kernel launch");
-  if (rc) return rc;
+// Fixed-tree reduce of the workspace's partials in `mode`.
+int run_reduce(const MlpArgs& a, void* ws, int P, vggt3::ReduceMode mode, float* dst, float lr, float* loss_out,
+               hipStream_t s) {
   const WsLayout l = ws_layout(a, P);
   const float* part = reinterpret_cast<const float*>(static_cast<const char*>(ws) + l.part);
   const float* loss_part = reinterpret_cast<const float*>(static_cast<const char*>(ws) + l.loss);
   return check_hip(vggt3::launch_reduce(part, loss_part, a.H, P, 3 * a.d * a.m, mode, dst, lr, loss_out, s),
                    "reduction kernel launch");
 }
+
+// Gradient over all tokens into (part, loss_part) then reduce in `mode`.
+int run_grad(const void* K, const void* Vp, const float* theta, const MlpArgs& a, void* ws, int P, int32_t loss,
+             vggt3::ReduceMode mode, float* dst, float lr, float* loss_out, hipStream_t s) {
+  int rc = check_hip(launch_partials(K, Vp, theta, a, ws, P, loss, loss_out != nullptr, s),
+                     "gradient kernel launch");
+  if (rc) return rc;
+  return run_reduce(a, ws, P, mode, dst, lr, loss_out, s);
+}
+
+// Divisor for v_mul_hi division of values below 2^16 (0 stands for 1).
+uint32_t div_magic(uint32_t d) { return d == 1 ? 0u : (uint32_t)(((1ull << 32) + d - 1) / d); }
 
 int check_workspace(const MlpArgs& a, const void* ws, size_t ws_bytes, int* P) {
   const size_t need = workspace_bytes(a, P);
@@ -533,6 +542,92 @@ int vggt3_ttt_write_noalloc(const void* K, const void* Vp, float* theta, int64_t
   }
   return vggt3_ttt_write_ex(K, Vp, theta, n_tokens, n_heads, d_head, d_hidden, lr, steps, loss, optimizer,
                             ns_steps, dtype, ws, need, loss_out, stream);
+}
+
+int vggt3_ttt_write_conv(const void* K, const void* V, const float* conv_w, int64_t n_views, int32_t grid_h,
+                         int32_t grid_w, int32_t n_special, float* theta, int32_t n_heads, int32_t d_head,
+                         int32_t d_hidden, float lr, int32_t steps, int32_t loss, int32_t optimizer,
+                         int32_t ns_steps, void* Vp_out, void* workspace, size_t workspace_bytes_, float* loss_out,
+                         void* stream) {
+  if (n_views < 0 || grid_h < 1 || grid_w < 1 || n_special < 0)
+    return fail(VGGT3_EINVAL, "bad layout: n_views %lld, grid %dx%d, n_special %d", (long long)n_views, grid_h,
+                grid_w, n_special);
+  const int64_t tpv = (int64_t)n_special + (int64_t)grid_h * grid_w;
+  if (tpv + 31 >= (1 << 16))
+    return fail(VGGT3_EUNSUPPORTED, "%lld tokens per view; the fused conv takes at most %d", (long long)tpv,
+                (1 << 16) - 32);
+  if (grid_w > vggt3::conv_fused_max_grid_w())
+    return fail(VGGT3_EUNSUPPORTED, "grid_w %d exceeds the fused conv's %d", grid_w, vggt3::conv_fused_max_grid_w());
+  if (n_views > ((int64_t)1 << 40) / tpv) return fail(VGGT3_EUNSUPPORTED, "too many tokens");
+  const MlpArgs a{n_views * tpv, n_heads, d_head, d_hidden, VGGT3_BF16};
+  int rc = check_write_args(a, K, V, theta, lr, steps, loss, optimizer, ns_steps, loss_out);
+  if (rc) return rc;
+  if (d_head != 64 || d_hidden != 128)
+    return fail(VGGT3_EUNSUPPORTED, "the fused conv write takes (d_head, d_hidden) = (64, 128), not (%d, %d)", d_head,
+                d_hidden);
+  int P = 1;
+  rc = check_workspace(a, workspace, workspace_bytes_, &P);
+  if (rc) return rc;
+  if (a.n > 0) {
+    if (conv_w == nullptr) return fail(VGGT3_EINVAL, "conv_w is NULL");
+    if (!aligned16(conv_w) || (Vp_out && !aligned16(Vp_out))) return fail(VGGT3_EINVAL, "pointer not 16-byte aligned");
+  }
+  const size_t tb = theta_bytes(a), xb = token_bytes(a), wb = (size_t)a.H * a.d * 9 * sizeof(float);
+  const size_t lb = loss_out ? (size_t)steps * n_heads * sizeof(float) : 0;
+  const size_t vb = Vp_out ? xb : 0;
+  const void* ins[] = {K, V, conv_w};
+  const size_t inb[] = {xb, xb, wb};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(theta, tb, ins[i], inb[i]) || overlap(loss_out, lb, ins[i], inb[i]) ||
+        overlap(workspace, workspace_bytes_, ins[i], inb[i]) || overlap(Vp_out, vb, ins[i], inb[i]))
+      return fail(VGGT3_EINVAL, "an output overlaps K, V or conv_w");
+  }
+  if (overlap(theta, tb, workspace, workspace_bytes_) || overlap(theta, tb, loss_out, lb) ||
+      overlap(theta, tb, Vp_out, vb) || overlap(loss_out, lb, workspace, workspace_bytes_) ||
+      overlap(loss_out, lb, Vp_out, vb) || overlap(Vp_out, vb, workspace, workspace_bytes_))
+    return fail(VGGT3_EINVAL, "theta, loss_out, V' and the workspace must not overlap");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.n == 0) {
+    if (loss_out) {
+      rc = check_hip(vggt3::launch_fill(loss_out, 0.0f, (int64_t)steps * n_heads, s), "fill launch");
+      if (rc) return rc;
+    }
+    return ok();
+  }
+  vggt3::ConvGeom geo;
+  geo.tpv = (int)tpv;
+  geo.n_special = n_special;
+  geo.grid_h = grid_h;
+  geo.grid_w = grid_w;
+  geo.magic_tpv = div_magic((uint32_t)tpv);
+  geo.magic_gw = div_magic((uint32_t)grid_w);
+  const WsLayout l = ws_layout(a, P);
+  char* base = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(base + l.part);
+  float* loss_part = reinterpret_cast<float*>(base + l.loss);
+  float* gbuf = reinterpret_cast<float*>(base + l.grad);
+  const bool dot = loss == VGGT3_LOSS_DOT;
+  for (int st = 0; st < steps; ++st) {
+    float* lrow = loss_out ? loss_out + (size_t)st * n_heads : nullptr;
+    if (st == 0 || Vp_out == nullptr)
+      rc = check_hip(vggt3::launch_grad_partial_conv_bf16(K, V, conv_w, st == 0 ? Vp_out : nullptr, geo, theta, part,
+                                                          loss_part, a.n, a.H, P, dot, lrow != nullptr, s),
+                     "fused conv gradient kernel launch");
+    else
+      rc = check_hip(vggt3::launch_grad_partial_bf16(K, Vp_out, theta, part, loss_part, a.n, a.H, P, dot,
+                                                     lrow != nullptr, s),
+                     "gradient kernel launch");
+    if (rc) return rc;
+    if (optimizer == VGGT3_OPT_GD) {
+      rc = run_reduce(a, workspace, P, vggt3::kApply, theta, lr, lrow, s);
+    } else {
+      rc = run_reduce(a, workspace, P, vggt3::kStore, gbuf, 0.0f, lrow, s);
+      if (!rc)
+        rc = check_hip(vggt3::launch_muon_apply(theta, gbuf, lr, a.H, a.d, a.m, ns_steps, s), "muon launch");
+    }
+    if (rc) return rc;
+  }
+  return ok();
 }
 
 int vggt3_ttt_grad_ex(const void* K, const void* Vp, const float* theta, float* grad, int32_t accumulate,

@@ -35,6 +35,15 @@ hipError_t launch_shortconv(const void* V, void* Vp, const float* w, int64_t n_v
 hipError_t launch_shortconv_k(const void* V, void* Vp, const float* w, int64_t n_views, int grid_h, int grid_w,
                               int n_special, int C, int ksize, bool bf16, hipStream_t stream);
 
+// Patch-grid geometry for the ShortConv2D fused into the gradient pass: each
+// view is n_special tokens, then grid_h x grid_w patch tokens row by row
+// (tpv tokens in all). magic_* = ceil(2^32 / divisor), 0 for a divisor of 1,
+// so that v_mul_hi divides any value below 2^16 exactly.
+struct ConvGeom {
+  int tpv, n_special, grid_h, grid_w;
+  uint32_t magic_tpv, magic_gw;
+};
+
 // Per-(head, chunk) fp32 gradient and loss partials.
 // part: [n_heads][P][3*d*m], loss_part: [n_heads][P]. dot selects the
 // dot-product loss -sum T(k).v' instead of sum (1/d)||T(k) - v'||^2.
@@ -42,6 +51,15 @@ hipError_t launch_shortconv_k(const void* V, void* Vp, const float* w, int64_t n
 hipError_t launch_grad_partial_bf16(const void* K, const void* Vp, const float* theta, float* part,
                                     float* loss_part, int64_t n_tokens, int n_heads, int P, bool dot, bool loss,
                                     hipStream_t stream);
+// The same partials with V' = ShortConv2D(V) formed inside the pass (bf16,
+// d = 64, m = 128, 3x3 filters conv_w [C][3][3] fp32, grid_w at most
+// conv_fused_max_grid_w(), n_tokens a whole number of views, tpv + 31 < 2^16).
+// Vp_out, if not NULL, receives V' (bf16, like K).
+int conv_fused_max_grid_w();
+hipError_t launch_grad_partial_conv_bf16(const void* K, const void* V, const float* conv_w, void* Vp_out,
+                                         const ConvGeom& geo, const float* theta, float* part, float* loss_part,
+                                         int64_t n_tokens, int n_heads, int P, bool dot, bool loss,
+                                         hipStream_t stream);
 hipError_t launch_grad_partial_f32(const void* K, const void* Vp, const float* theta, float* part,
                                    float* loss_part, int64_t n_tokens, int n_heads, int d, int m, int P,
                                    bool dot, hipStream_t stream);

@@ -45,6 +45,18 @@
 // of them architectural VGPRs, so MFMA results need no copies before VALU use)
 // so that two workgroups share a CU: while one waits at a barrier or on LDS,
 // the other's MFMA and VALU work fills the SIMDs. All LDS addressing is 32-bit.
+//
+// FUSE: the ShortConv2D in front of the write ("Non-Linear Spatial Mixing via
+// ShortConv2D", same section) is computed inside this pass, so V' never has
+// to exist in HBM: the kernel reads V, keeps a ring of 128 token rows of the
+// head's channels in LDS, and each thread forms V' of one token and 8
+// channels by the conv kernel's contract (same bits as the conv kernel).
+// With VOUT it also stores that V'. The ring, the filters and a zero row take
+// the place of the transposed W_d copy (the Y phase then reads W_d^T with
+// transposing loads). The conv is about 250 vector instructions per thread
+// and tile on top of the pass's own, which the MFMA work does not hide: at
+// 1000 views the fused pass takes about 1.3 ms longer than the plain one, as
+// long as the separate conv pass, so the split form remains the faster one.
 #include "bf16_ops.hpp"
 #include "kernels.hpp"
 
@@ -74,16 +86,34 @@ constexpr int YP = 36;               // pitch of Y[o][t]: a lane stores its 4 to
 constexpr int KV_BUFS = 2;
 constexpr int TSZ = T * TP;          // elements per token tile
 
-// LDS map (elements of bf16).
-constexpr int OFF_K = 0;
-constexpr int OFF_V = OFF_K + KV_BUFS * TSZ;
-constexpr int OFF_Y = OFF_V + KV_BUFS * TSZ;
-constexpr int OFF_H = OFF_Y + TSZ;
-constexpr int OFF_W = OFF_H + M * HPT;
 constexpr int WTP = M + 8;             // pitch of W_d^T[o][hid]
-constexpr int OFF_WT = OFF_W + M * WP;
-constexpr int LDS_ELEMS = OFF_WT + D * WTP;
-static_assert(LDS_ELEMS * 2 <= 80 * 1024, "two workgroups per CU");
+
+// Fused ShortConv2D: V (not V') streams through a ring of RING_TOK token rows
+// of this head's 64 channels (128 bytes each, unpadded), indexed by the token
+// index modulo RING_TOK; a zero row after it stands in for out-of-grid taps;
+// the head's 3x3 filters sit beside it as fp32 [tap][channel].
+constexpr int RING_TOK = 128;
+constexpr int OFF_RING = 0;
+constexpr int OFF_ZERO = OFF_RING + RING_TOK * D;
+constexpr int OFF_CW = OFF_ZERO + D;            // fp32, 2 elements each
+constexpr int FUSE_BASE = OFF_CW + 2 * 9 * D;
+constexpr int CONV_MAX_W = 47;  // widest grid row whose 3x3 window fits the ring (see the staging order)
+
+// LDS map (elements of bf16). The fused form drops the transposed W_d copy
+// to make room for the ring and reads W_d^T with transposing loads instead.
+template <bool FUSE>
+struct LdsMap {
+  static constexpr int K = FUSE ? FUSE_BASE : 0;
+  static constexpr int V = K + KV_BUFS * TSZ;
+  static constexpr int Y = V + KV_BUFS * TSZ;
+  static constexpr int H = Y + TSZ;
+  static constexpr int W = H + M * HPT;
+  static constexpr int WT = W + M * WP;
+  static constexpr int ELEMS = FUSE ? WT : WT + D * WTP;
+};
+static_assert(LdsMap<false>::ELEMS * 2 <= 80 * 1024, "two workgroups per CU");
+static_assert(LdsMap<true>::ELEMS * 2 <= 80 * 1024, "two workgroups per CU");
+static_assert(FUSE_BASE % 8 == 0, "16-byte aligned tiles");
 static_assert(64 * YP <= TSZ, "Y tile");
 
 typedef __attribute__((address_space(3))) uint16_t lu16;
@@ -110,12 +140,14 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <bool DOT, bool LOSS>
+template <bool DOT, bool LOSS, bool FUSE, bool VOUT>
 __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
     const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg, const float* __restrict__ theta,
     float* __restrict__ part, float* __restrict__ loss_part, int64_t n_tokens, int n_heads, int P,
-    int64_t n_blocks) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[LDS_ELEMS];
+    int64_t n_blocks, const float* __restrict__ cw, uint16_t* __restrict__ Vpo, ConvGeom geo) {
+  typedef LdsMap<FUSE> Map;
+  constexpr int OFF_K = Map::K, OFF_V = Map::V, OFF_Y = Map::Y, OFF_H = Map::H, OFF_W = Map::W, OFF_WT = Map::WT;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[Map::ELEMS];
   __shared__ float red[4];
   lu16* const lds = (lu16*)smem;
 
@@ -165,12 +197,23 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
         pack_bf16x2(Wd[hid * D + o], Wd[hid * D + o + 1]);
   }
   // and transposed, [o][hid], for the Y phase's B operand.
-  if (!DOT) {
+  if (!DOT && !FUSE) {
     for (int idx = tid; idx < M * D / 2; idx += 256) {
       const int o = (2 * idx) / M, hid = (2 * idx) % M;
       *(__attribute__((address_space(3))) uint32_t*)(lds + OFF_WT + o * WTP + hid) =
           pack_bf16x2(Wd[hid * D + o], Wd[(hid + 1) * D + o]);
     }
+  }
+
+  typedef __attribute__((address_space(3))) float lf32;
+  typedef __attribute__((address_space(3))) f32x4 lf32x4;
+  lf32* const cwl = (lf32*)(lds + OFF_CW);
+  if constexpr (FUSE) {
+    for (int idx = tid; idx < 9 * D; idx += 256) {
+      const int tap = idx / D, ch = idx % D;
+      cwl[idx] = cw[((int64_t)head * D + ch) * 9 + tap];
+    }
+    if (tid < 8) lst16(lds + OFF_ZERO + 8 * tid, u32x4{0u, 0u, 0u, 0u});
   }
 
   f32x16 accWd[2], accWg[2], accWu[2];
@@ -192,6 +235,7 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
   const int o_hst = (32 * w + l32) * HPT + 4 * hh;          // H stores
   const int o_ha = (8 * g4 + jr) * HPT + 16 * tb + 4 * q4;  // Y phase: H^T reads (A operand)
   const int o_wtb = (16 * ob + i16) * WTP + 8 * g4;         // Y phase: W_d^T reads (B operand)
+  const int o_wtr = (8 * g4 + jr) * WP + 16 * ob + 4 * q4;  // fused form: the same by transposing W_d reads
   const int o_vl = (16 * tb + 4 * g4 + jr) * TP + 16 * ob + 4 * q4;  // Y phase: -V' at the C positions
   const int o_yst = (16 * ob + i16) * YP + 16 * tb + 4 * g4;         // Y stores: 4 tokens of one output
   const int o_ytr = (8 * hh + jr) * YP + cb + 4 * q4;                // dH phase: Y^T transpose reads
@@ -206,6 +250,14 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
   const int srow = tid >> 3, scol = (tid & 7) * 8;
   const int o_stage = srow * TP + scol;
   const int lane_off = (srow * (int)C + scol) * 2;
+  auto load_k = [&](int i, u32x4& kr) {
+    const int64_t t0 = (tile_begin + i) * T;
+    const int64_t off = t0 * C + (int64_t)head * D;
+    const int64_t range = (n_tokens - t0) * C * 2 - (int64_t)head * D * 2;
+    const int nrec = (int)(range > 0x7fffffffLL ? 0x7fffffffLL : (range > 0 ? range : 0));
+    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + off), (short)0, nrec, 0x00020000);
+    kr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, lane_off, 0, 0));
+  };
   auto load_tile = [&](int i, u32x4& kr, u32x4& vr) {
     const int64_t t0 = (tile_begin + i) * T;
     const int64_t off = t0 * C + (int64_t)head * D;
@@ -220,15 +272,128 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
   auto store_tile = [&](int i, const u32x4& kr, const u32x4& vr) {
     const int buf = i % KV_BUFS;
     lst16(lds + OFF_K + buf * TSZ + o_stage, kr);
-    lst16(lds + OFF_V + buf * TSZ + o_stage, vr ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u});
+    if constexpr (!FUSE)
+      lst16(lds + OFF_V + buf * TSZ + o_stage, vr ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u});
   };
 
+  // Fused form. V tile u holds tokens t_c - 48 + 32u .. + 31 (t_c: the chunk's
+  // first token). Before the first tile, V tiles 0..3 are staged and V'(0) is
+  // computed from them. body(i) stages V tile i + 4 right after its first
+  // barrier (over rows that only V'(i), computed before that barrier, read)
+  // and computes V'(i + 1) after its second barrier, at the end of the tile:
+  // the ring then holds tokens [t_c + 32i - 16, t_c + 32i + 112), and the
+  // window of V'(i + 1), tokens t_c + 32(i + 1) - w - 1 .. t_c + 32(i + 1) + 31
+  // + w + 1 with w = grid_w <= CONV_MAX_W, lies inside it.
+  const int64_t t_c = tile_begin * T;
+  auto load_v = [&](int u, u32x4& vr) {
+    const int64_t t0 = t_c - 48 + 32 * (int64_t)u;
+    const int64_t tb = t0 < 0 ? 0 : t0;  // before token 0: rows with negative offsets read as zeros
+    const int64_t off = tb * C + (int64_t)head * D;
+    const int64_t range = (n_tokens - tb) * C * 2 - (int64_t)head * D * 2;
+    const int nrec = (int)(range > 0x7fffffffLL ? 0x7fffffffLL : (range > 0 ? range : 0));
+    const int voff = lane_off + (t0 < 0 ? (int)(t0 * C * 2) : 0);
+    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + off), (short)0, nrec, 0x00020000);
+    vr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, voff, 0, 0));
+  };
+  auto stage_v = [&](int u, const u32x4& vr) {
+    const int r0 = (int)((t_c - 48 + 32 * (int64_t)u) & (RING_TOK - 1));
+    lst16(lds + OFF_RING + ((r0 + srow) & (RING_TOK - 1)) * D + scol, vr);
+  };
+  // V'(j) of this lane's token and 8 channels by the conv contract: acc = +0,
+  // taps row offset outermost, column offset innermost, acc = fl(acc + fl(w v))
+  // with no fused multiply-add; out-of-grid taps read the zero row (adding
+  // fl(w * 0) = +-0 leaves acc unchanged, as skipping them would); special
+  // tokens pass V through; rows at or past n_tokens stage zeros.
+  auto conv_tile = [&](int j, uint32_t cpos) {
+    const int64_t t0 = (tile_begin + j) * T;
+    const int64_t left = n_tokens - t0;
+    const bool valid = srow < (left > T ? T : (int)left);
+    const uint32_t p = cpos + (uint32_t)srow;
+    const uint32_t q = geo.magic_tpv ? __umulhi(p, geo.magic_tpv) : p;
+    const int pos = (int)(p - q * (uint32_t)geo.tpv);
+    const bool special = pos < geo.n_special;
+    const uint32_t pp = (uint32_t)(pos - geo.n_special);
+    const uint32_t yy = geo.magic_gw ? __umulhi(pp, geo.magic_gw) : pp;
+    const int y = (int)yy, x = (int)(pp - yy * (uint32_t)geo.grid_w);
+    const bool up = y > 0, dn = y < geo.grid_h - 1, lf = x > 0, rt = x < geo.grid_w - 1;
+    const uint32_t c7 = (uint32_t)((int)(t0 & (RING_TOK - 1)) + srow) << 7;
+    const uint32_t oc16 = (uint32_t)scol * 2;
+    const uint32_t zaddr = (uint32_t)(RING_TOK * 128) + oc16;
+    const __attribute__((address_space(3))) uint8_t* ring = (const __attribute__((address_space(3))) uint8_t*)(lds + OFF_RING);
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    u32x4 center = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int dy = 0; dy < 3; ++dy) {
+#pragma unroll
+      for (int dx = 0; dx < 3; ++dx) {
+        const int off = (dy - 1) * geo.grid_w + (dx - 1);
+        uint32_t a = ((c7 + (uint32_t)(off * 128)) & (uint32_t)((RING_TOK - 1) << 7)) | oc16;
+        bool ok = true;
+        if (dy == 0) ok = up;
+        if (dy == 2) ok = dn;
+        if (dx == 0) ok = ok && lf;
+        if (dx == 2) ok = ok && rt;
+        if (dy != 1 || dx != 1) a = ok ? a : zaddr;
+        const u32x4 v = *(const lu32x4*)(ring + a);
+        if (dy == 1 && dx == 1) center = v;
+        const int tap = 3 * dy + dx;
+        const f32x4 w0 = *(const lf32x4*)(cwl + tap * D + scol);
+        const f32x4 w1 = *(const lf32x4*)(cwl + tap * D + scol + 4);
+        {
+#pragma clang fp contract(off)
+          acc[0] = acc[0] + w0[0] * bf16_lo(v[0]);
+          acc[1] = acc[1] + w0[1] * bf16_hi(v[0]);
+          acc[2] = acc[2] + w0[2] * bf16_lo(v[1]);
+          acc[3] = acc[3] + w0[3] * bf16_hi(v[1]);
+          acc[4] = acc[4] + w1[0] * bf16_lo(v[2]);
+          acc[5] = acc[5] + w1[1] * bf16_hi(v[2]);
+          acc[6] = acc[6] + w1[2] * bf16_lo(v[3]);
+          acc[7] = acc[7] + w1[3] * bf16_hi(v[3]);
+        }
+      }
+    }
+    u32x4 res = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                 pack_bf16x2(acc[6], acc[7])};
+    if (special) res = center;
+    if (!valid) res = u32x4{0u, 0u, 0u, 0u};
+    lst16(lds + OFF_V + (j % KV_BUFS) * TSZ + o_stage, res ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u});
+    if constexpr (VOUT) {
+      const int64_t off = t0 * C + (int64_t)head * D;
+      const int64_t range = left * C * 2 - (int64_t)head * D * 2;
+      const int nrec = (int)(range > 0x7fffffffLL ? 0x7fffffffLL : (range > 0 ? range : 0));
+      const __amdgpu_buffer_rsrc_t ores = __builtin_amdgcn_make_buffer_rsrc((void*)(Vpo + off), (short)0, nrec, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b128(res, ores, lane_off, 0, 0);
+    }
+  };
+  uint32_t cpos = 0;  // position within its view of the first token of the tile being convolved
+  if constexpr (FUSE) cpos = (uint32_t)(t_c % geo.tpv);
+
   u32x4 kr0, vr0, kr1, vr1;
-  if (nt > 0) {
-    load_tile(0, kr0, vr0);
+  if constexpr (!FUSE) {
+    if (nt > 0) {
+      load_tile(0, kr0, vr0);
+      store_tile(0, kr0, vr0);
+      load_tile(1, kr1, vr1);
+      load_tile(2, kr0, vr0);
+    }
+  } else if (nt > 0) {
+    load_k(0, kr0);
     store_tile(0, kr0, vr0);
-    load_tile(1, kr1, vr1);
-    load_tile(2, kr0, vr0);
+    u32x4 va, vb, vc, vd;
+    load_v(0, va);
+    load_v(1, vb);
+    load_v(2, vc);
+    load_v(3, vd);
+    stage_v(0, va);
+    stage_v(1, vb);
+    stage_v(2, vc);
+    stage_v(3, vd);
+    __syncthreads();  // V tiles 0..3 and the filters staged
+    conv_tile(0, cpos);
+    load_k(1, kr1);
+    load_v(4, vr1);
+    load_k(2, kr0);
+    load_v(5, vr0);
   }
 
   lu16* const Yt = lds + OFF_Y;
@@ -236,6 +401,10 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
     const lu16* Kc = lds + OFF_K + (i % KV_BUFS) * TSZ;
     const lu16* Vc = lds + OFF_V + (i % KV_BUFS) * TSZ;
     __syncthreads();  // B0: tile i staged; everything of tile i-1 consumed
+    if constexpr (FUSE) {
+      stage_v(i + 4, vrs);  // over rows the window of V'(i) (computed before B0) was the last to read
+      load_v(i + 6, vrs);
+    }
 
     // G, U (tokens x this wave's hidden units): element r is token
     // 8(r/4) + 4hh + r%4, hidden unit 32w + l32.
@@ -275,8 +444,9 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
     }
     // Stage tile i+1 (loaded two tiles ago) and start loading i+3 into its registers.
     if (i + 1 < nt) store_tile(i + 1, krs, vrs);
-    load_tile(i + 3, krs, vrs);
-    if (!DOT) __syncthreads();  // B1: H(i) complete
+    if constexpr (FUSE) load_k(i + 3, krs);
+    else load_tile(i + 3, krs, vrs);
+    if (!DOT || FUSE) __syncthreads();  // B1: H(i) complete; the conv window of V'(i+1) read
 
     // Y (tokens 16tb.., outputs 16(ob+b)..) = H W_d over all hidden units;
     // R = Y - V'; Y -> LDS [t][o].
@@ -288,7 +458,12 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
         const bf16x8 ha = ltr_op(hp, hp + 4 * HPT);
 #pragma unroll
         for (int b = 0; b < 2; ++b)
-          accY[b] = mfma16(ha, lop(lds + OFF_WT + o_wtb + 16 * b * WTP + 32 * ks), accY[b]);
+          if constexpr (FUSE) {
+            const lu16* wp = lds + OFF_W + o_wtr + 32 * ks * WP + 16 * b;
+            accY[b] = mfma16(ha, ltr_op(wp, wp + 4 * WP), accY[b]);
+          } else {
+            accY[b] = mfma16(ha, lop(lds + OFF_WT + o_wtb + 16 * b * WTP + 32 * ks), accY[b]);
+          }
       }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -362,6 +537,15 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
         accWu[eb] = mfma32(kA, dUop[ks], accWu[eb]);
       }
     }
+    // V'(i + 1) into the slot tile i-1 released, from the ring as staged
+    // before B1.
+    if constexpr (FUSE) {
+      if (i + 1 < nt) {
+        cpos += T;
+        while (cpos >= (uint32_t)geo.tpv) cpos -= (uint32_t)geo.tpv;
+        conv_tile(i + 1, cpos);
+      }
+    }
   };
   // Whole pairs in the loop (no conditional body, so the compiler's load waits
   // stay exact across iterations), an odd last tile after it.
@@ -406,11 +590,37 @@ hipError_t launch_grad_partial_bf16(const void* K, const void* Vp, const float* 
                                     float* loss_part, int64_t n_tokens, int n_heads, int P, bool dot, bool loss,
                                     hipStream_t stream) {
   const int64_t n_blocks = (int64_t)n_heads * P;
-  auto kernel = dot ? (loss ? grad_partial_bf16_kernel<true, true> : grad_partial_bf16_kernel<true, false>)
-                    : (loss ? grad_partial_bf16_kernel<false, true> : grad_partial_bf16_kernel<false, false>);
+  auto kernel = dot ? (loss ? grad_partial_bf16_kernel<true, true, false, false>
+                            : grad_partial_bf16_kernel<true, false, false, false>)
+                    : (loss ? grad_partial_bf16_kernel<false, true, false, false>
+                            : grad_partial_bf16_kernel<false, false, false, false>);
   hipLaunchKernelGGL(kernel, dim3((unsigned)n_blocks), dim3(256), 0, stream, static_cast<const uint16_t*>(K),
-                     static_cast<const uint16_t*>(Vp), theta, part, loss_part, n_tokens, n_heads, P, n_blocks);
+                     static_cast<const uint16_t*>(Vp), theta, part, loss_part, n_tokens, n_heads, P, n_blocks,
+                     nullptr, nullptr, ConvGeom{});
+  return hipGetLastError();
+}
+
+int conv_fused_max_grid_w() { return CONV_MAX_W; }
+
+hipError_t launch_grad_partial_conv_bf16(const void* K, const void* V, const float* conv_w, void* Vp_out,
+                                         const ConvGeom& geo, const float* theta, float* part, float* loss_part,
+                                         int64_t n_tokens, int n_heads, int P, bool dot, bool loss,
+                                         hipStream_t stream) {
+  const int64_t n_blocks = (int64_t)n_heads * P;
+  typedef void (*kfn)(const uint16_t*, const uint16_t*, const float*, float*, float*, int64_t, int, int, int64_t,
+                      const float*, uint16_t*, ConvGeom);
+  kfn kernel;
+  if (Vp_out)
+    kernel = dot ? (loss ? grad_partial_bf16_kernel<true, true, true, true> : grad_partial_bf16_kernel<true, false, true, true>)
+                 : (loss ? grad_partial_bf16_kernel<false, true, true, true> : grad_partial_bf16_kernel<false, false, true, true>);
+  else
+    kernel = dot ? (loss ? grad_partial_bf16_kernel<true, true, true, false> : grad_partial_bf16_kernel<true, false, true, false>)
+                 : (loss ? grad_partial_bf16_kernel<false, true, true, false> : grad_partial_bf16_kernel<false, false, true, false>);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)n_blocks), dim3(256), 0, stream, static_cast<const uint16_t*>(K),
+                     static_cast<const uint16_t*>(V), theta, part, loss_part, n_tokens, n_heads, P, n_blocks, conv_w,
+                     static_cast<uint16_t*>(Vp_out), geo);
   return hipGetLastError();
 }
 
 }  // namespace vggt3
+

@@ -300,3 +300,34 @@ def test_wide_mlp_shape_rules(lib):
     # the workspace must not overlap the token inputs
     assert lib.vggt3_ttt_grad(FAKE, FAKE2, FAKE3, big_ptr, 0, n, 1, d, m, tla.BF16, FAKE, ws, None,
                               None) == tla.EINVAL
+
+
+def test_write_conv_validation(lib):
+    nv, gh, gw, ns, H = 2, 37, 37, 5, 16
+    n = nv * (ns + gh * gw)
+    ws_need = lib.vggt3_ttt_workspace_bytes(n, H, 64, 128, tla.BF16)
+    CW = ctypes.c_void_p(0x50000000)
+    WS = ctypes.c_void_p(0x60000000)
+
+    def call(K=FAKE, V=FAKE2, w=CW, nv=nv, gh=gh, gw=gw, ns=ns, theta=FAKE3, H=H, d=64, m=128, lr=0.1, steps=2,
+             loss=0, opt=0, nsteps=5, vp=None, ws=WS, wsb=ws_need, lo=None):
+        return lib.vggt3_ttt_write_conv(K, V, w, nv, gh, gw, ns, theta, H, d, m, lr, steps, loss, opt, nsteps, vp, ws,
+                                        wsb, lo, None)
+
+    assert call(gw=48) == tla.EUNSUPPORTED and "47" in _err(lib)  # the ring holds a 47-wide window
+    assert call(ns=70000) == tla.EUNSUPPORTED
+    assert call(d=16, m=32) == tla.EUNSUPPORTED
+    assert call(d=1024, m=4096, H=1) == tla.EUNSUPPORTED
+    assert call(nv=-1) == tla.EINVAL
+    assert call(gh=0) == tla.EINVAL
+    assert call(ns=-1) == tla.EINVAL
+    assert call(steps=0) == tla.EINVAL
+    assert call(loss=7) == tla.EINVAL
+    assert call(w=None) == tla.EINVAL
+    assert call(w=ctypes.c_void_p(0x50000004)) == tla.EINVAL  # misaligned filters
+    assert call(vp=ctypes.c_void_p(0x20000000)) == tla.EINVAL and "overlap" in _err(lib)  # V' over V
+    assert call(vp=ctypes.c_void_p(0x70000008)) == tla.EINVAL  # misaligned V'
+    assert call(ws=None) == tla.EWORKSPACE
+    assert call(wsb=ws_need - 1) == tla.EWORKSPACE
+    assert call(theta=CW) == tla.EINVAL and "overlap" in _err(lib)
+    assert call(nv=0, K=None, V=None, w=None, ws=None, wsb=0) == tla.OK  # empty scene, nothing enqueued
