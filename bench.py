@@ -335,11 +335,6 @@ def wide_bench(args, loss_kind, opt_kind, recipe_desc):
     }
     if args.offload > 0:
         res["offload"] = offload_bench(tla, inp, Vp, cfg, args, loss_kind, opt_kind)
-    if args.conv_fused:
-        if cfg.dtype != "bf16" or args.conv_variant != "v3":
-            raise SystemExit("--conv-fused takes the bf16 workloads with the 3x3 conv on V")
-        res["conv_fused"] = conv_fused_bench(tla, inp, cfg, args, loss_kind, opt_kind, ws, O)
-        res["conv_fused"]["split_conv_and_write_ms"] = conv_ms + write_ms
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, cfg, loss=loss_kind, opt=opt_kind)
     print(json.dumps(res), flush=True)
@@ -543,6 +538,11 @@ def main():
     }
     if args.offload > 0:
         res["offload"] = offload_bench(tla, inp, Vp, cfg, args, loss_kind, opt_kind)
+    if args.conv_fused:
+        if cfg.dtype != "bf16" or args.conv_variant != "v3":
+            raise SystemExit("--conv-fused takes the bf16 workloads with the 3x3 conv on V")
+        res["conv_fused"] = conv_fused_bench(tla, inp, cfg, args, loss_kind, opt_kind, ws, O)
+        res["conv_fused"]["split_conv_and_write_ms"] = conv_ms + write_ms
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, cfg, loss=loss_kind, opt=opt_kind)
     print(json.dumps(res), flush=True)
