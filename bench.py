@@ -38,7 +38,8 @@ SPEC_CLOCK_GHZ = 2.4
 COUNTER_CLOCK_GHZ = round(SPEC_CLOCK_GHZ * 2.815 / 3.762, 2)
 PEAK_HBM_GBS = 8000.0
 METRIC = "TTT-layer tokens/sec (write+read) at 1000 views; % bf16 MFMA peak"
-GRAD_KERNEL = "grad_partial_bf16_kernel"
+# The gradient kernel each recipe's timed write steps launch (no loss value).
+GRAD_KERNEL = {"mse": "grad_partial_mse_pipe_kernel", "dot": "grad_partial_bf16_kernel<dot>"}
 GRAD_SOURCE = os.path.join(ROOT, "test_layer_amd", "csrc", "ttt_write_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grad_partial_bf16_views1000_traffic.json")
 
@@ -514,7 +515,8 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": GRAD_KERNEL,
+            "kernel": (("grad_partial_bf16_kernel" + ("<dot>" if loss_kind == "dot" else "") + " (with loss value)")
+                       if args.with_loss else GRAD_KERNEL[loss_kind]),
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

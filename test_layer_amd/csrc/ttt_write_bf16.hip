@@ -46,6 +46,13 @@
 // so that two workgroups share a CU: while one waits at a barrier or on LDS,
 // the other's MFMA and VALU work fills the SIMDs. All LDS addressing is 32-bit.
 //
+// The squared-error pass without the loss value (the write step's own case)
+// runs grad_partial_mse_pipe_kernel instead: the same arithmetic, software-
+// pipelined so that each wave's SwiGLU of tile c is interleaved with its
+// weight-gradient MFMAs of tile c-1 (a wave overlaps its own vector and MFMA
+// instructions, while vector-only and MFMA-only phases of different waves
+// hardly overlap), with K, V' in three-slot rings and two barriers per tile.
+//
 // FUSE: the ShortConv2D in front of the write ("Non-Linear Spatial Mixing via
 // ShortConv2D", same section) is computed inside this pass, so V' never has
 // to exist in HBM: the kernel reads V, keeps a ring of 128 token rows of the
@@ -114,6 +121,20 @@ struct LdsMap {
 static_assert(LdsMap<false>::ELEMS * 2 <= 80 * 1024, "two workgroups per CU");
 static_assert(LdsMap<true>::ELEMS * 2 <= 80 * 1024, "two workgroups per CU");
 static_assert(FUSE_BASE % 8 == 0, "16-byte aligned tiles");
+
+// LDS map of the software-pipelined squared-error kernel: K and -V' in rings
+// of three slots.
+struct PipeMap {
+  static constexpr int KV_BUFS = 3;
+  static constexpr int K = 0;
+  static constexpr int V = K + KV_BUFS * TSZ;
+  static constexpr int Y = V + KV_BUFS * TSZ;
+  static constexpr int H = Y + TSZ;
+  static constexpr int W = H + M * HPT;
+  static constexpr int WT = W + M * WP;
+  static constexpr int ELEMS = WT + D * WTP;
+};
+static_assert(PipeMap::ELEMS * 2 <= 80 * 1024, "two workgroups per CU");
 static_assert(64 * YP <= TSZ, "Y tile");
 
 typedef __attribute__((address_space(3))) uint16_t lu16;
@@ -138,6 +159,15 @@ __device__ __forceinline__ bf16x8 ltr_op(const lu16* p0, const lu16* p1) {
 //   C/D:       lane l, register r holds C[row = 4*(l/16) + r][col = l%16]
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Workgroup barrier that the compiler's scheduler may not move any
+// instruction across (by default it moves register-only work such as MFMAs
+// freely past s_barrier, which would undo a hand-laid instruction mix).
+__device__ __forceinline__ void segment_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <bool DOT, bool LOSS, bool FUSE, bool VOUT>
@@ -584,19 +614,381 @@ __global__ __launch_bounds__(256, 2) void grad_partial_bf16_kernel(
     loss_part[(int64_t)head * P + chunk] = ((red[0] + red[1]) + (red[2] + red[3])) * (DOT ? 1.0f : 1.0f / D);
 }
 
+// The squared-error gradient without the loss value (what a write step with
+// no loss output needs), software-pipelined across tiles. Same partials, bit
+// for bit, as grad_partial_bf16_kernel<false, false, false, false>: every
+// accumulator receives the same MFMA terms in the same order.
+__global__ __launch_bounds__(256, 2) void grad_partial_mse_pipe_kernel(
+    const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg, const float* __restrict__ theta,
+    float* __restrict__ part, float* __restrict__ loss_part, int64_t n_tokens, int n_heads, int P,
+    int64_t n_blocks) {
+  constexpr int KV_BUFS = PipeMap::KV_BUFS;
+  constexpr int OFF_K = PipeMap::K, OFF_V = PipeMap::V, OFF_Y = PipeMap::Y, OFF_H = PipeMap::H, OFF_W = PipeMap::W,
+                OFF_WT = PipeMap::WT;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[PipeMap::ELEMS];
+  lu16* const lds = (lu16*)smem;
+
+  const int64_t blk = xcd_remap(blockIdx.x, n_blocks);
+  const int head = (int)(blk / P);
+  const int chunk = (int)(blk % P);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;               // k-half of a 32x32x16 operand
+  const int g4 = lane >> 4;               // k-quarter of a 16x16x32 operand
+  const int i16 = lane & 15;
+  const int cb = 16 * ((lane >> 4) & 1);  // column base of this lane's 16-lane group (32-wide reads)
+  const int jr = (lane & 15) >> 2;        // transpose-read source row within the group
+  const int q4 = lane & 3;                // transpose-read source column quad
+  const int64_t C = (int64_t)n_heads * D;
+  const int tb = w >> 1;                  // this wave's Y rows: tokens 16tb..16tb+15
+  const int ob = 2 * (w & 1);             // and Y column blocks ob, ob+1 (16 outputs each)
+
+  const float* th = theta + (int64_t)head * PER_HEAD;
+  const float* Wg = th;
+  const float* Wu = th + DM;
+  const float* Wd = th + 2 * DM;
+
+  // W_g / W_u operands in registers: B[k = e][j = hid], e = 16ks + 8hh + jj, hid = 32w + l32.
+  bf16x8 WgB[4], WuB[4];
+  {
+    const int hid = 32 * w + l32;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float g[8], u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = 16 * ks + 8 * hh + j;
+        g[j] = Wg[e * M + hid];
+        u[j] = Wu[e * M + hid];
+      }
+      WgB[ks] = pack8(g);
+      WuB[ks] = pack8(u);
+    }
+  }
+  // W_d (bf16) in LDS, natural [hid][o] layout.
+  for (int idx = tid; idx < M * D / 2; idx += 256) {
+    const int hid = (2 * idx) / D, o = (2 * idx) % D;
+    *(__attribute__((address_space(3))) uint32_t*)(lds + OFF_W + hid * WP + o) =
+        pack_bf16x2(Wd[hid * D + o], Wd[hid * D + o + 1]);
+  }
+  // and transposed, [o][hid], for the Y phase's B operand.
+  for (int idx = tid; idx < M * D / 2; idx += 256) {
+    const int o = (2 * idx) / M, hid = (2 * idx) % M;
+    *(__attribute__((address_space(3))) uint32_t*)(lds + OFF_WT + o * WTP + hid) =
+        pack_bf16x2(Wd[hid * D + o], Wd[(hid + 1) * D + o]);
+  }
+
+  f32x16 accWd[2], accWg[2], accWu[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    accWd[i] = f32x16{};
+    accWg[i] = f32x16{};
+    accWu[i] = f32x16{};
+  }
+  const int64_t n_tiles_all = (n_tokens + T - 1) / T;
+  const int64_t tile_begin = n_tiles_all * chunk / P;
+  const int nt = (int)(n_tiles_all * (chunk + 1) / P - tile_begin);
+
+  // Lane-constant LDS offsets (elements).
+  const int o_row = l32 * TP + 8 * hh;                     // token-row operand reads (b128)
+  const int o_tr = (4 * hh + jr) * TP + cb + 4 * q4;        // transpose reads over token rows
+  const int o_hst = (32 * w + l32) * HPT + 4 * hh;          // H stores
+  const int o_ha = (8 * g4 + jr) * HPT + 16 * tb + 4 * q4;  // Y phase: H^T reads (A operand)
+  const int o_wtb = (16 * ob + i16) * WTP + 8 * g4;         // Y phase: W_d^T reads (B operand)
+  const int o_yst = (16 * ob + i16) * YP + 16 * tb + 4 * g4;         // Y stores: 4 tokens of one output
+  const int o_ytr = (8 * hh + jr) * YP + cb + 4 * q4;                // dH phase: Y^T transpose reads
+  const int o_wrow = (32 * w + l32) * WP + 8 * hh;          // W_d rows of this wave's units
+
+  // Tile staging: thread -> row tid>>3, 8 channels at (tid&7)*8. K and V'
+  // are read through buffer descriptors built per tile from 64-bit scalar
+  // arithmetic: based at the tile's first token and this head, with a range
+  // that ends at the tensor's end. The lane offset is fixed; rows at or past
+  // n_tokens lie beyond the range and read as zeros, which also keeps the loads
+  // unconditional, so the compiler's load-counter waits stay exact.
+  const int srow = tid >> 3, scol = (tid & 7) * 8;
+  const int o_stage = srow * TP + scol;
+  const int lane_off = (srow * (int)C + scol) * 2;
+  auto load_tile = [&](int i, u32x4& kr, u32x4& vr) {
+    const int64_t t0 = (tile_begin + i) * T;
+    const int64_t off = t0 * C + (int64_t)head * D;
+    const int64_t range = (n_tokens - t0) * C * 2 - (int64_t)head * D * 2;  // bytes to the tensor's end
+    const int nrec = (int)(range > 0x7fffffffLL ? 0x7fffffffLL : (range > 0 ? range : 0));
+    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + off), (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + off), (short)0, nrec, 0x00020000);
+    kr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, lane_off, 0, 0));
+    vr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, lane_off, 0, 0));
+  };
+  // V' is staged negated (rows past the end become -0, which adds nothing).
+  auto store_tile = [&](int buf, const u32x4& kr, const u32x4& vr) {
+    lst16(lds + OFF_K + buf * TSZ + o_stage, kr);
+    lst16(lds + OFF_V + buf * TSZ + o_stage, vr ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u});
+  };
+
+  u32x4 kr0, vr0, kr1, vr1;
+  lu16* const Yt = lds + OFF_Y;
+
+  // Carried from one tile to the next: the previous tile's weight-gradient operands.
+  bf16x8 HopP[2], dGopP[2], dUopP[2];
+
+  // G, U (tokens x this wave's hidden units) of tile i from K(i) in LDS:
+  // element r is token 8(r/4) + 4hh + r%4, hidden unit 32w + l32.
+  auto gate_up = [&](int sl, f32x16& accG, f32x16& accU) {
+    const lu16* Kc = lds + OFF_K + sl * TSZ;
+    accG = f32x16{};
+    accU = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 a = lop(Kc + o_row + 16 * ks);
+      accG = mfma32(a, WgB[ks], accG);
+      accU = mfma32(a, WuB[ks], accU);
+    }
+  };
+
+  // Weight gradients of tile i from its carried operands (k-slot jj of k-step
+  // ks is token 16ks + 8(jj/4) + 4hh + jj%4, the register order of C tiles),
+  // as a fixed sequence of 8 MFMA steps per k-step ks: gW_d block 0 against Y
+  // then -V', block 1 likewise, then gW_g, gW_u against K block 0, then block
+  // 1. Each accumulator sees its terms in the same order as in
+  // grad_partial_bf16_kernel, so the partials are bitwise the same.
+  constexpr int WG_STEPS = 16;
+  constexpr int PER_KS = WG_STEPS / 2;
+  // LDS operand of step k (the B operand of a gW_d step, the K operand of a
+  // gW_g step; a gW_u step reuses the K operand of the step before it).
+  auto wg_reuses = [](int k) { const int j = k % PER_KS; return j >= PER_KS - 4 && (j - (PER_KS - 4)) % 2 == 1; };
+  auto wg_operand = [&](int sl, int k) -> bf16x8 {
+    const lu16* Kc = lds + OFF_K + sl * TSZ;
+    const lu16* Vc = lds + OFF_V + sl * TSZ;
+    const int ks = k / PER_KS, j = k % PER_KS;
+    if (j < PER_KS - 4) {  // gW_d step
+      const int nb = j / 2;
+      if (j % 2 == 0) {
+        const lu16* yt = Yt + (32 * nb + l32) * YP + 16 * ks + 4 * hh;
+        const u32x2 y0 = *(const lu32x2*)yt, y1 = *(const lu32x2*)(yt + 8);
+        return as_bf16x8(u32x4{y0[0], y0[1], y1[0], y1[1]});
+      }
+      const lu16* vt = Vc + o_tr + 16 * ks * TP + 32 * nb;
+      return ltr_op(vt, vt + 8 * TP);
+    }
+    const int eb = (j - (PER_KS - 4)) / 2;
+    const lu16* kt = Kc + o_tr + 16 * ks * TP + 32 * eb;
+    return ltr_op(kt, kt + 8 * TP);
+  };
+  auto wg_mfma = [&](int k, const bf16x8& op) {
+    const int ks = k / PER_KS, j = k % PER_KS;
+    if (j < PER_KS - 4) {
+      const int nb = j / 2;
+      accWd[nb] = mfma32(HopP[ks], op, accWd[nb]);
+    } else {
+      const int e = j - (PER_KS - 4), eb = e / 2;
+      if (e % 2 == 0) accWg[eb] = mfma32(op, dGopP[ks], accWg[eb]);
+      else accWu[eb] = mfma32(op, dUopP[ks], accWu[eb]);
+    }
+  };
+  auto weight_grads = [&](int i) {
+#pragma unroll
+    for (int k = 0; k < WG_STEPS; ++k) {
+      const bf16x8 op = wg_operand(i % KV_BUFS, wg_reuses(k) ? k - 1 : k);
+      wg_mfma(k, op);
+    }
+  };
+
+  // One tile, software-pipelined so that each wave's instruction stream mixes
+  // matrix and vector work: the SwiGLU of tile i (vector ALU) is interleaved
+  // with the weight-gradient MFMAs of tile i-1, which do not depend on it.
+  //   A | G, U(i) ; SwiGLU(i) -> H(i) with weight grads(i-1) ; stage K,V'(i+1), load i+3
+  //   B1| Y(i) = H(i) W_d (16x16x32 tiles over all hidden units) ; Y -> LDS [o][t]
+  //   B2| dH(i) = (Y - V') W_d^T ; dG, dU
+  // K and V' tiles live in a ring of three LDS slots: tile i-1 is read in A
+  // while tile i+1 is written there, tile i stays for B1/B2.
+  // On one SIMD, vector instructions overlap an MFMA of the same wave almost
+  // for free, while a wave of only vector work beside a wave of only MFMAs
+  // slows both down. Segment A is therefore laid out by hand: the SwiGLU runs
+  // in four groups of four elements (stage by stage within a group, so that
+  // consecutive instructions are independent), cut into one chunk per MFMA;
+  // each MFMA's LDS operand is read two MFMAs ahead; sched_barrier fences keep
+  // the compiler from regrouping the chunks.
+  // sl = i % KV_BUFS, passed as a literal so that every slot offset folds
+  // into the LDS instructions' immediate offsets.
+  auto body = [&](int i, int sl, u32x4& krs, u32x4& vrs, bool first) __attribute__((always_inline)) {
+    const int slp = (sl + KV_BUFS - 1) % KV_BUFS, sln = (sl + 1) % KV_BUFS;
+    const lu16* Vc = lds + OFF_V + sl * TSZ;
+    f32x16 accG, accU;
+    gate_up(sl, accG, accU);
+    bf16x8 opr[WG_STEPS];
+    if (!first) {
+      opr[0] = wg_operand(slp, 0);
+      opr[1] = wg_operand(slp, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // SwiGLU: s = sigmoid(G), A = G s, H = A U, gp = U silu'(G) = U s + H (1 - s),
+    // with sigmoid(g) = 1 / (1 + 2^(-g log2 e)). A and gp stay in fp32
+    // registers until the backward step.
+    float Af[16], GPf[16], Hf[16], X[16];
+    uint32_t Hpk[8];
+    constexpr int OPS = 34;  // per group of four elements: 8 stages x 4, then 2 packs
+    auto sw_op = [&](int grp, int o) {
+      if (o >= 32) {
+        const int r = 4 * grp + 2 * (o - 32);
+        Hpk[r / 2] = pack_bf16x2(Hf[r], Hf[r + 1]);
+        return;
+      }
+      const int r = 4 * grp + o % 4;
+      const float g = accG[r], u = accU[r];
+      switch (o / 4) {
+        case 0: X[r] = g * -1.4426950408889634f; break;
+        case 1: X[r] = __builtin_amdgcn_exp2f(X[r]); break;
+        case 2: X[r] = 1.0f + X[r]; break;
+        case 3: X[r] = __builtin_amdgcn_rcpf(X[r]); break;
+        case 4: Af[r] = g * X[r]; break;
+        case 5: Hf[r] = Af[r] * u; break;
+        case 6: GPf[r] = fmaf(u, X[r], Hf[r]); break;
+        default: GPf[r] = fmaf(-Hf[r], X[r], GPf[r]); break;
+      }
+    };
+    constexpr int MPG = WG_STEPS / 4;  // MFMAs per group
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+#pragma unroll
+      for (int c = 0; c < MPG; ++c) {
+        const int k = grp * MPG + c;
+        if (!first) {
+          if (k + 2 < WG_STEPS && !wg_reuses(k + 2)) opr[k + 2] = wg_operand(slp, k + 2);
+          wg_mfma(k, opr[wg_reuses(k) ? k - 1 : k]);
+        }
+#pragma unroll
+        for (int o = c * OPS / MPG; o < (c + 1) * OPS / MPG; ++o) sw_op(grp, o);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    bf16x8 Hop[2];
+    Hop[0] = as_bf16x8(u32x4{Hpk[0], Hpk[1], Hpk[2], Hpk[3]});
+    Hop[1] = as_bf16x8(u32x4{Hpk[4], Hpk[5], Hpk[6], Hpk[7]});
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      lu16* hp = lds + OFF_H + o_hst + 16 * ks;
+      lst8(hp, u32x2{Hpk[4 * ks], Hpk[4 * ks + 1]});
+      lst8(hp + 8, u32x2{Hpk[4 * ks + 2], Hpk[4 * ks + 3]});
+    }
+    // Stage tile i+1 (loaded two tiles ago) and start loading i+3 into its registers.
+    if (i + 1 < nt) store_tile(sln, krs, vrs);
+    load_tile(i + 3, krs, vrs);
+    segment_barrier();  // B1: H(i) and K,V'(i+1) staged; tile i-1 and Y(i-1) consumed
+
+    // Y (tokens 16tb.., outputs 16(ob+b)..) = H W_d over all hidden units;
+    // Y -> LDS [o][t].
+    {
+      f32x4 accY[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const lu16* hp = lds + OFF_H + o_ha + 32 * ks * HPT;
+        const bf16x8 ha = ltr_op(hp, hp + 4 * HPT);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          accY[b] = mfma16(ha, lop(lds + OFF_WT + o_wtb + 16 * b * WTP + 32 * ks), accY[b]);
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const uint32_t y01 = pack_bf16x2(accY[b][0], accY[b][1]);
+        const uint32_t y23 = pack_bf16x2(accY[b][2], accY[b][3]);
+        lst8(Yt + o_yst + 16 * b * YP, u32x2{y01, y23});
+      }
+      segment_barrier();  // B2: Y(i) complete
+    }
+
+    // dH = (Y - V') W_d^T for this wave's hidden units; dU = dH A, dG = dH gp.
+    {
+      f32x16 accH = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 wdt = lop(lds + OFF_W + o_wrow + 16 * ks);  // B[k = o][j = hid]
+        const lu16* yp = Yt + o_ytr + 16 * ks * YP;
+        accH = mfma32(ltr_op(yp, yp + 4 * YP), wdt, accH);
+        accH = mfma32(lop(Vc + o_row + 16 * ks), wdt, accH);
+      }
+      float dg[16], du[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        du[r] = accH[r] * Af[r];
+        dg[r] = accH[r] * GPf[r];
+      }
+      dGopP[0] = pack8(&dg[0]);
+      dGopP[1] = pack8(&dg[8]);
+      dUopP[0] = pack8(&du[0]);
+      dUopP[1] = pack8(&du[8]);
+      HopP[0] = Hop[0];
+      HopP[1] = Hop[1];
+    }
+  };
+
+  if (nt > 0) {
+    load_tile(0, kr0, vr0);
+    store_tile(0, kr0, vr0);
+    load_tile(1, kr1, vr1);
+    load_tile(2, kr0, vr0);
+    segment_barrier();  // K, V'(0) staged
+    body(0, 0, kr1, vr1, true);
+  }
+  // Six tiles per iteration (two register sets x three LDS slots, so every
+  // slot offset is a constant), no conditional body inside the loop; the
+  // remaining tiles after it.
+  int i = 1;
+  for (; i + 5 < nt; i += 6) {
+    body(i, 1, kr0, vr0, false);
+    body(i + 1, 2, kr1, vr1, false);
+    body(i + 2, 0, kr0, vr0, false);
+    body(i + 3, 1, kr1, vr1, false);
+    body(i + 4, 2, kr0, vr0, false);
+    body(i + 5, 0, kr1, vr1, false);
+  }
+  if (i < nt) body(i, 1, kr0, vr0, false);
+  if (i + 1 < nt) body(i + 1, 2, kr1, vr1, false);
+  if (i + 2 < nt) body(i + 2, 0, kr0, vr0, false);
+  if (i + 3 < nt) body(i + 3, 1, kr1, vr1, false);
+  if (i + 4 < nt) body(i + 4, 2, kr0, vr0, false);
+  if (nt > 0) weight_grads(nt - 1);
+
+  // Partials in theta layout, times 2/d.
+  constexpr float kScale = 2.0f / D;
+  float* out = part + ((int64_t)head * P + chunk) * PER_HEAD;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int hid = 32 * w + row;  // gW_d rows
+      const int o = 32 * b + l32;
+      out[2 * DM + hid * D + o] = accWd[b][r] * kScale;
+      const int e = 32 * b + row;    // gW_g / gW_u rows
+      const int hc = 32 * w + l32;
+      out[e * M + hc] = accWg[b][r] * kScale;
+      out[DM + e * M + hc] = accWu[b][r] * kScale;
+    }
+  }
+  if (tid == 0) loss_part[(int64_t)head * P + chunk] = __builtin_nanf("");
+}
+
+
 }  // namespace
 
 hipError_t launch_grad_partial_bf16(const void* K, const void* Vp, const float* theta, float* part,
                                     float* loss_part, int64_t n_tokens, int n_heads, int P, bool dot, bool loss,
                                     hipStream_t stream) {
   const int64_t n_blocks = (int64_t)n_heads * P;
+  const uint16_t* Kb = static_cast<const uint16_t*>(K);
+  const uint16_t* Vb = static_cast<const uint16_t*>(Vp);
+  if (!dot && !loss) {
+    hipLaunchKernelGGL(grad_partial_mse_pipe_kernel, dim3((unsigned)n_blocks), dim3(256), 0, stream, Kb, Vb, theta,
+                       part, loss_part, n_tokens, n_heads, P, n_blocks);
+    return hipGetLastError();
+  }
   auto kernel = dot ? (loss ? grad_partial_bf16_kernel<true, true, false, false>
                             : grad_partial_bf16_kernel<true, false, false, false>)
-                    : (loss ? grad_partial_bf16_kernel<false, true, false, false>
-                            : grad_partial_bf16_kernel<false, false, false, false>);
-  hipLaunchKernelGGL(kernel, dim3((unsigned)n_blocks), dim3(256), 0, stream, static_cast<const uint16_t*>(K),
-                     static_cast<const uint16_t*>(Vp), theta, part, loss_part, n_tokens, n_heads, P, n_blocks,
-                     nullptr, nullptr, ConvGeom{});
+                    : grad_partial_bf16_kernel<false, true, false, false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)n_blocks), dim3(256), 0, stream, Kb, Vb, theta, part, loss_part, n_tokens,
+                     n_heads, P, n_blocks, nullptr, nullptr, ConvGeom{});
   return hipGetLastError();
 }
 
