@@ -35,8 +35,10 @@
  *     Within a scene, tokens are grouped by view, and each view is
  *     [n_special special tokens][grid_h*grid_w patch tokens, row-major].
  *   - dtype VGGT3_BF16: token tensors are bfloat16, MLP contractions run on
- *     bf16 MFMA with fp32 accumulation. dtype VGGT3_F32: token tensors are
- *     float32 and all arithmetic is fp32.
+ *     bf16 MFMA with fp32 accumulation (at the small (16, 32) head shape the
+ *     bf16 inputs are widened exactly and the arithmetic is fp32, with O
+ *     rounded to bf16). dtype VGGT3_F32: token tensors are float32 and all
+ *     arithmetic is fp32.
  *   - Fast weights theta are float32 [n_heads][3*d_head*d_hidden]; per head the
  *     three row-major blocks W_g [d_head][d_hidden], W_u [d_head][d_hidden],
  *     W_d [d_hidden][d_head].
@@ -155,8 +157,8 @@ size_t vggt3_ttt_workspace_bytes(int64_t n_tokens, int32_t n_heads, int32_t d_he
  *             (may be NULL when that is 0).
  *   loss_out  NULL or float32 [steps][n_heads]: the loss at the theta each
  *             step starts from.
- * Supported (d_head, d_hidden): bf16 (64, 128); f32 (16, 32) and (64, 128);
- * and bf16 (1024, 4096) with n_heads = 1, the pages' full-width MLP ([GRAPH]
+ * Supported (d_head, d_hidden): bf16 (64, 128) and (16, 32); f32 (16, 32) and
+ * (64, 128); and bf16 (1024, 4096) with n_heads = 1, the pages' full-width MLP ([GRAPH]
  * "TTT MLP Architecture and Inner Optimization": one 1024 -> 4096 -> 1024
  * SwiGLU), with either loss and either update (vggt3_ttt_write_ex). Its
  * workspace holds the intermediates of one chunk of up to 131,072 tokens

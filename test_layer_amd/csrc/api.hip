@@ -52,13 +52,26 @@ bool is_wide(int32_t d, int32_t m) { return d == vggt3::wide::kD && m == vggt3::
 
 // Shapes the library has kernels for.
 bool supported_mlp(int32_t dt, int32_t d, int32_t m) {
-  if (dt == VGGT3_BF16) return (d == 64 && m == 128) || is_wide(d, m);
+  if (dt == VGGT3_BF16) return (d == 64 && m == 128) || (d == 16 && m == 32) || is_wide(d, m);
   if (dt == VGGT3_F32) return (d == 16 && m == 32) || (d == 64 && m == 128);
   return false;
 }
 
-// Token tile of the gradient kernel of each dtype (the unit of the Eq. 5 chunking).
-int tile_tokens(int32_t dt) { return dt == VGGT3_BF16 ? vggt3::kGradTileBf16 : vggt3::kGradTileF32; }
+// The fp32 vector kernels serve the fp32 mode and, with bf16 token tensors,
+// the bf16 (16, 32) shape (too narrow for the 32-wide MFMA tiles).
+bool f32_kernels(int32_t dt, int32_t d, int32_t m) { return dt == VGGT3_F32 || (d == 16 && m == 32); }
+
+// Token tile of the gradient kernel that serves (dtype, d, m): the unit of the
+// Eq. 5 chunking.
+int tile_tokens(int32_t dt, int32_t d, int32_t m) {
+  return f32_kernels(dt, d, m) ? vggt3::kGradTileF32 : vggt3::kGradTileBf16;
+}
+
+hipError_t launch_read_any(const void* Q, const float* theta, void* O, int64_t n, int32_t H, int32_t d, int32_t m,
+                           int32_t dt, hipStream_t s) {
+  return f32_kernels(dt, d, m) ? vggt3::launch_read_f32(Q, theta, O, n, H, d, m, dt == VGGT3_BF16, s)
+                               : vggt3::launch_read_bf16(Q, theta, O, n, H, s);
+}
 
 struct MlpArgs {
   int64_t n;
@@ -145,7 +158,7 @@ size_t workspace_bytes(const MlpArgs& a, int* P_out) {
     if (P_out) *P_out = 1;
     return a.n == 0 ? 0 : wide_ws(a.n).total;
   }
-  const int P = vggt3::ttt_num_chunks(a.n, a.H, tile_tokens(a.dt));
+  const int P = vggt3::ttt_num_chunks(a.n, a.H, tile_tokens(a.dt, a.d, a.m));
   if (P_out) *P_out = P;
   if (a.n == 0) return 0;
   return ws_layout(a, P).total;
@@ -284,9 +297,10 @@ hipError_t launch_partials(const void* K, const void* Vp, const float* theta, co
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.part);
   float* loss_part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.loss);
   const bool dot = loss == VGGT3_LOSS_DOT;
-  if (a.dt == VGGT3_BF16)
+  if (!f32_kernels(a.dt, a.d, a.m))
     return vggt3::launch_grad_partial_bf16(K, Vp, theta, part, loss_part, a.n, a.H, P, dot, want_loss, s);
-  return vggt3::launch_grad_partial_f32(K, Vp, theta, part, loss_part, a.n, a.H, a.d, a.m, P, dot, s);
+  return vggt3::launch_grad_partial_f32(K, Vp, theta, part, loss_part, a.n, a.H, a.d, a.m, P, dot,
+                                        a.dt == VGGT3_BF16, s);
 }
 
 // Fixed-tree reduce of the workspace's partials in `mode`.
@@ -830,8 +844,7 @@ int vggt3_ttt_read(const void* Q, const float* theta, void* O, int64_t n_tokens,
   const size_t tb = theta_bytes(a), xb = token_bytes(a);
   if (overlap(O, xb, Q, xb) || overlap(O, xb, theta, tb)) return fail(VGGT3_EINVAL, "O overlaps Q or theta");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dtype == VGGT3_BF16 ? vggt3::launch_read_bf16(Q, theta, O, a.n, a.H, s)
-                                     : vggt3::launch_read_f32(Q, theta, O, a.n, a.H, a.d, a.m, s);
+  hipError_t e = launch_read_any(Q, theta, O, a.n, a.H, a.d, a.m, dtype, s);
   rc = check_hip(e, "read kernel launch");
   return rc ? rc : ok();
 }
@@ -929,7 +942,7 @@ int vggt3_ttt_write_streamed(const void* K_host, const void* Vp_host, float* the
   const int64_t nc = (a.n + ct - 1) / ct;
   const int64_t tail = a.n - (nc - 1) * ct;
   if (!wide && ws_layout(MlpArgs{tail, n_heads, d_head, d_hidden, dtype},
-                         vggt3::ttt_num_chunks(tail, n_heads, tile_tokens(dtype)))
+                         vggt3::ttt_num_chunks(tail, n_heads, tile_tokens(dtype, d_head, d_hidden)))
                        .grad > ws_layout(ca, P).grad)
     return fail(VGGT3_EUNSUPPORTED, "internal: tail chunk layout exceeds the workspace");
 
@@ -976,7 +989,8 @@ int vggt3_ttt_write_streamed(const void* K_host, const void* Vp_host, float* the
         rc = wide_grad(Kd, Vd, theta, ta, loss, workspace, wl, c == 0 ? vggt3::kStore : vggt3::kAccum, gacc, 0.0f,
                        lrow, c > 0 ? 1 : 0, s);
       else
-        rc = run_grad(Kd, Vd, theta, ta, workspace, vggt3::ttt_num_chunks(tn, n_heads, tile_tokens(dtype)), loss,
+        rc = run_grad(Kd, Vd, theta, ta, workspace,
+                      vggt3::ttt_num_chunks(tn, n_heads, tile_tokens(dtype, d_head, d_hidden)), loss,
                       c == 0 ? vggt3::kStore : vggt3::kAccum, gacc, 0.0f, lrow, s);
       if (!rc && cs != s) rc = check_hip(hipEventRecord(freed[sl], s), "event record");
       if (rc) return rc;
@@ -1073,9 +1087,7 @@ int vggt3_ttt_read_streamed_ex(const void* Q_host, const float* theta, void* O_h
     if (wide) {
       rc = wide_read(q_slot(c), theta, o_slot(c), MlpArgs{tn, n_heads, d_head, d_hidden, dtype}, workspace, wl, s);
     } else {
-      hipError_t e = dtype == VGGT3_BF16 ? vggt3::launch_read_bf16(q_slot(c), theta, o_slot(c), tn, n_heads, s)
-                                         : vggt3::launch_read_f32(q_slot(c), theta, o_slot(c), tn, n_heads, d_head,
-                                                                  d_hidden, s);
+      hipError_t e = launch_read_any(q_slot(c), theta, o_slot(c), tn, n_heads, d_head, d_hidden, dtype, s);
       rc = check_hip(e, "read kernel launch");
     }
     if (!rc) rc = check_hip(hipEventRecord(done[sl], s), "event record");

@@ -60,9 +60,10 @@ hipError_t launch_grad_partial_conv_bf16(const void* K, const void* V, const flo
                                          const ConvGeom& geo, const float* theta, float* part, float* loss_part,
                                          int64_t n_tokens, int n_heads, int P, bool dot, bool loss,
                                          hipStream_t stream);
+// fp32 arithmetic; bf16_tokens: K and V' are bf16 (only at d = 16, m = 32).
 hipError_t launch_grad_partial_f32(const void* K, const void* Vp, const float* theta, float* part,
                                    float* loss_part, int64_t n_tokens, int n_heads, int d, int m, int P,
-                                   bool dot, hipStream_t stream);
+                                   bool dot, bool bf16_tokens, hipStream_t stream);
 
 // Muon update theta -= lr * NS(grad) for every per-head weight matrix, NS the
 // `ns_steps`-step quintic Newton-Schulz orthogonalisation (fp32).
@@ -83,6 +84,6 @@ hipError_t launch_fill(float* dst, float value, int64_t count, hipStream_t strea
 hipError_t launch_read_bf16(const void* Q, const float* theta, void* O, int64_t n_tokens, int n_heads,
                             hipStream_t stream);
 hipError_t launch_read_f32(const void* Q, const float* theta, void* O, int64_t n_tokens, int n_heads,
-                           int d, int m, hipStream_t stream);
+                           int d, int m, bool bf16_tokens, hipStream_t stream);
 
 }  // namespace vggt3

@@ -8,6 +8,10 @@
 // entirely in fp32 on the vector ALUs. This path serves the fp32 mode (tight
 // tolerances, small heads); it stages the head's weights and every per-tile
 // intermediate in LDS and lets each thread own a fixed set of outputs.
+// With BF the token tensors (K, V', Q, O) are bf16: they are widened exactly
+// on load and O is rounded to bf16 (ties to even) on store; the arithmetic
+// stays fp32. This serves the bf16 mode at the small (16, 32) head shape,
+// whose per-head tiles are too narrow for the 32-wide MFMA kernels.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,9 +29,16 @@ struct F32Cfg {
 
 __device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
-template <int D, int M, bool DOT>
-__global__ __launch_bounds__(256, 1) void grad_partial_f32_kernel(const float* __restrict__ K,
-                                                                const float* __restrict__ Vp,
+// Token element i of a bf16 (BF) or fp32 tensor, as fp32.
+template <bool BF>
+__device__ __forceinline__ float ld_tok(const void* p, int64_t i) {
+  if constexpr (BF) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+  else return static_cast<const float*>(p)[i];
+}
+
+template <int D, int M, bool DOT, bool BF>
+__global__ __launch_bounds__(256, 1) void grad_partial_f32_kernel(const void* __restrict__ K,
+                                                                const void* __restrict__ Vp,
                                                                 const float* __restrict__ theta,
                                                                 float* __restrict__ part,
                                                                 float* __restrict__ loss_part,
@@ -67,8 +78,8 @@ __global__ __launch_bounds__(256, 1) void grad_partial_f32_kernel(const float* _
       const int t = i / D, c = i % D;
       const int64_t tok = tok0 + t;
       const bool ok = tok < n_tokens;
-      Ks[i] = ok ? K[tok * C + (int64_t)head * D + c] : 0.0f;
-      Vs[i] = ok ? Vp[tok * C + (int64_t)head * D + c] : 0.0f;
+      Ks[i] = ok ? ld_tok<BF>(K, tok * C + (int64_t)head * D + c) : 0.0f;
+      Vs[i] = ok ? ld_tok<BF>(Vp, tok * C + (int64_t)head * D + c) : 0.0f;
     }
     __syncthreads();
     for (int i = tid; i < TT * M; i += 256) {
@@ -141,10 +152,10 @@ __global__ __launch_bounds__(256, 1) void grad_partial_f32_kernel(const float* _
     loss_part[(int64_t)head * P + chunk] = ((red[0] + red[1]) + (red[2] + red[3])) * (DOT ? 1.0f : 1.0f / D);
 }
 
-template <int D, int M>
-__global__ __launch_bounds__(256) void read_f32_kernel(const float* __restrict__ Q,
+template <int D, int M, bool BF>
+__global__ __launch_bounds__(256) void read_f32_kernel(const void* __restrict__ Q,
                                                         const float* __restrict__ theta,
-                                                        float* __restrict__ O, int64_t n_tokens,
+                                                        void* __restrict__ O, int64_t n_tokens,
                                                         int n_heads, int P, int64_t n_blocks) {
   using Cfg = F32Cfg<D, M>;
   constexpr int TT = 32, DM = Cfg::DM, PER_HEAD = Cfg::PER_HEAD;
@@ -168,7 +179,7 @@ __global__ __launch_bounds__(256) void read_f32_kernel(const float* __restrict__
     const int64_t tok0 = tile * TT;
     for (int i = tid; i < TT * D; i += 256) {
       const int64_t tok = tok0 + i / D;
-      Qs[i] = tok < n_tokens ? Q[tok * C + (int64_t)head * D + i % D] : 0.0f;
+      Qs[i] = tok < n_tokens ? ld_tok<BF>(Q, tok * C + (int64_t)head * D + i % D) : 0.0f;
     }
     __syncthreads();
     for (int i = tid; i < TT * M; i += 256) {
@@ -186,35 +197,39 @@ __global__ __launch_bounds__(256) void read_f32_kernel(const float* __restrict__
       const int64_t tok = tok0 + t;
       float y = 0.0f;
       for (int j = 0; j < M; ++j) y = fmaf(Hs[t * M + j], Wd[j * D + o], y);
-      if (tok < n_tokens) O[tok * C + (int64_t)head * D + o] = y;
+      if (tok < n_tokens) {
+        const int64_t at = tok * C + (int64_t)head * D + o;
+        if constexpr (BF) static_cast<uint16_t*>(O)[at] = f32_to_bf16_bits(y);
+        else static_cast<float*>(O)[at] = y;
+      }
     }
     __syncthreads();
   }
 }
 
-template <int D, int M>
-hipError_t launch_grad_f32_t(const float* K, const float* Vp, const float* theta, float* part,
+template <int D, int M, bool BF>
+hipError_t launch_grad_f32_t(const void* K, const void* Vp, const float* theta, float* part,
                              float* loss_part, int64_t n_tokens, int n_heads, int P, bool dot,
                              hipStream_t stream) {
   const int64_t n_blocks = (int64_t)n_heads * P;
   if (dot)
-    hipLaunchKernelGGL((grad_partial_f32_kernel<D, M, true>), dim3((unsigned)n_blocks), dim3(256), 0, stream, K,
-                       Vp, theta, part, loss_part, n_tokens, n_heads, P, n_blocks);
+    hipLaunchKernelGGL((grad_partial_f32_kernel<D, M, true, BF>), dim3((unsigned)n_blocks), dim3(256), 0, stream,
+                       K, Vp, theta, part, loss_part, n_tokens, n_heads, P, n_blocks);
   else
-    hipLaunchKernelGGL((grad_partial_f32_kernel<D, M, false>), dim3((unsigned)n_blocks), dim3(256), 0, stream, K,
-                       Vp, theta, part, loss_part, n_tokens, n_heads, P, n_blocks);
+    hipLaunchKernelGGL((grad_partial_f32_kernel<D, M, false, BF>), dim3((unsigned)n_blocks), dim3(256), 0, stream,
+                       K, Vp, theta, part, loss_part, n_tokens, n_heads, P, n_blocks);
   return hipGetLastError();
 }
 
-template <int D, int M>
-hipError_t launch_read_f32_t(const float* Q, const float* theta, float* O, int64_t n_tokens, int n_heads,
+template <int D, int M, bool BF>
+hipError_t launch_read_f32_t(const void* Q, const float* theta, void* O, int64_t n_tokens, int n_heads,
                              hipStream_t stream) {
   const int64_t n_tiles = (n_tokens + 31) / 32;
   int64_t P = (512 + n_heads - 1) / n_heads;
   if (P > n_tiles) P = n_tiles;
   if (P < 1) P = 1;
   const int64_t n_blocks = (int64_t)n_heads * P;
-  hipLaunchKernelGGL((read_f32_kernel<D, M>), dim3((unsigned)n_blocks), dim3(256), 0, stream, Q, theta, O,
+  hipLaunchKernelGGL((read_f32_kernel<D, M, BF>), dim3((unsigned)n_blocks), dim3(256), 0, stream, Q, theta, O,
                      n_tokens, n_heads, (int)P, n_blocks);
   return hipGetLastError();
 }
@@ -223,22 +238,23 @@ hipError_t launch_read_f32_t(const float* Q, const float* theta, float* O, int64
 
 hipError_t launch_grad_partial_f32(const void* K, const void* Vp, const float* theta, float* part,
                                    float* loss_part, int64_t n_tokens, int n_heads, int d, int m, int P,
-                                   bool dot, hipStream_t stream) {
-  const float* k = static_cast<const float*>(K);
-  const float* v = static_cast<const float*>(Vp);
+                                   bool dot, bool bf16_tokens, hipStream_t stream) {
   if (d == 16 && m == 32)
-    return launch_grad_f32_t<16, 32>(k, v, theta, part, loss_part, n_tokens, n_heads, P, dot, stream);
-  if (d == 64 && m == 128)
-    return launch_grad_f32_t<64, 128>(k, v, theta, part, loss_part, n_tokens, n_heads, P, dot, stream);
+    return bf16_tokens
+               ? launch_grad_f32_t<16, 32, true>(K, Vp, theta, part, loss_part, n_tokens, n_heads, P, dot, stream)
+               : launch_grad_f32_t<16, 32, false>(K, Vp, theta, part, loss_part, n_tokens, n_heads, P, dot, stream);
+  if (d == 64 && m == 128 && !bf16_tokens)
+    return launch_grad_f32_t<64, 128, false>(K, Vp, theta, part, loss_part, n_tokens, n_heads, P, dot, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_read_f32(const void* Q, const float* theta, void* O, int64_t n_tokens, int n_heads, int d,
-                           int m, hipStream_t stream) {
-  const float* q = static_cast<const float*>(Q);
-  float* o = static_cast<float*>(O);
-  if (d == 16 && m == 32) return launch_read_f32_t<16, 32>(q, theta, o, n_tokens, n_heads, stream);
-  if (d == 64 && m == 128) return launch_read_f32_t<64, 128>(q, theta, o, n_tokens, n_heads, stream);
+                           int m, bool bf16_tokens, hipStream_t stream) {
+  if (d == 16 && m == 32)
+    return bf16_tokens ? launch_read_f32_t<16, 32, true>(Q, theta, O, n_tokens, n_heads, stream)
+                       : launch_read_f32_t<16, 32, false>(Q, theta, O, n_tokens, n_heads, stream);
+  if (d == 64 && m == 128 && !bf16_tokens)
+    return launch_read_f32_t<64, 128, false>(Q, theta, O, n_tokens, n_heads, stream);
   return hipErrorInvalidValue;
 }
 

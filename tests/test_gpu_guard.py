@@ -91,6 +91,7 @@ READ_CASES = [
     (997, 16, 64, 128, torch.bfloat16),
     (4122, 3, 64, 128, torch.bfloat16),
     (37, 2, 16, 32, torch.float32),
+    (37, 2, 16, 32, torch.bfloat16),  # the fp32 kernels with bf16 tokens
     (300, 4, 64, 128, torch.float32),
     (257, 1, 1024, 4096, torch.bfloat16),  # the full-width MLP
 ]
@@ -121,6 +122,7 @@ GRAD_CASES = [
     (33, 16, 64, 128, torch.bfloat16),
     (997, 16, 64, 128, torch.bfloat16),
     (37, 1, 16, 32, torch.float32),
+    (45, 2, 16, 32, torch.bfloat16),
     (301, 2, 64, 128, torch.float32),
     (257, 1, 1024, 4096, torch.bfloat16),
 ]

@@ -324,6 +324,46 @@ def test_tiny_f32_layer_parity():
     assert rel_err(to64(O), O_ref) <= TOL_F32
 
 
+@pytest.mark.parametrize("recipe", [("mse", "gd"), ("dot", "muon")], ids=lambda r: "_".join(r))
+def test_tiny_bf16_layer_parity(recipe):
+    """The (16, 32) head shape with bf16 token tensors: 2 views of 8x8 patches, 3
+    heads, 2 steps, then the read. The fp32 kernels serve it (exact widening of
+    the bf16 inputs, fp32 arithmetic), so the write meets the fp32 bar; the read's
+    output is rounded to bf16."""
+    from dataclasses import replace
+    cfg = replace(CONFIGS["tiny_f32"], dtype="bf16", n_heads=3, steps=2, normalize=True, name="tiny_bf16")
+    inp = make_inputs(cfg, DEV)
+    assert inp.K.dtype == torch.bfloat16
+    Vp = _conv(inp)
+    theta = inp.theta0.clone()
+    loss = torch.empty((cfg.steps, cfg.n_heads), device=DEV)
+    tla.ttt_write(inp.K, Vp, theta, cfg.lr, cfg.steps, cfg.n_heads, loss_out=loss, loss=recipe[0],
+                  optimizer=recipe[1])
+    O = tla.ttt_read(inp.Q, theta, cfg.n_heads)
+    th0 = inp.theta0.cpu().numpy()
+    Vp_ref = _oracle_conv(inp, "bf16").astype(np.float64)
+    np.testing.assert_array_equal(bits(Vp), f32_to_bits(Vp_ref.astype(np.float32), True))
+    th_ref, L_ref, _ = oracle.ttt_write(to64(inp.K), Vp_ref, th0, cfg.n_heads, 16, 32, cfg.lr, cfg.steps,
+                                        loss=recipe[0], opt=recipe[1])
+    th = theta.cpu().numpy().astype(np.float64)
+    err = rel_err_per_head(th, th_ref, cfg.n_heads, axis_cols=False).max()
+    ok, worst = dtheta_ok(th, th_ref, th0, cfg.n_heads, TOL_F32 if recipe[1] == "gd" else 1e-3, cfg.steps)
+    print(f"[bf16 16x32 {recipe}] theta {err:.2e}, delta-theta worst/allowance {worst:.2f}", flush=True)
+    assert err <= TOL_F32
+    assert ok, worst
+    if recipe[0] == "mse":
+        lerr = np.abs(loss.cpu().numpy() - L_ref) / np.abs(L_ref)
+        assert lerr.max() <= TOL_F32, lerr
+    O_ref = oracle.ttt_read(to64(inp.Q), th_ref, cfg.n_heads, 16, 32)
+    oerr = rel_err_per_head(to64(O), O_ref, cfg.n_heads).max()
+    print(f"[bf16 16x32 {recipe}] read {oerr:.2e}", flush=True)
+    assert oerr <= 4e-3  # one bf16 rounding of each output
+    g = tla.ttt_grad(inp.K, Vp, inp.theta0, cfg.n_heads, loss=recipe[0])
+    g_ref, _ = oracle.ttt_grad(to64(inp.K), Vp_ref, th0, cfg.n_heads, 16, 32, loss=recipe[0])
+    assert rel_err_per_head(to64(g).reshape(cfg.n_heads, -1), g_ref.reshape(cfg.n_heads, -1), cfg.n_heads,
+                            axis_cols=False).max() <= TOL_F32
+
+
 def test_f32_vggt_shape_parity():
     cfg = _small_vggt(views=2, heads=2, dtype="f32", steps=2)
     inp = make_inputs(cfg, DEV)
