@@ -16,16 +16,14 @@
 // are not staged yet (a strip's first block: the zero row above the grid and
 // rows 0..3; later blocks: the next 3 rows, or the zero row below the grid) with
 // direct global -> LDS loads (global_load_lds_dwordx4, one 64-lane instruction
-// per 1 KB of a row, with the streaming cache policy: sc0 and nt set, as V is
-// read once), so each input row is read from HBM once. Those loads for
+// per 1 KB of a row), so each input row is read from HBM once. Those loads for
 // block k + 1 are issued before block k is computed and fill ring slots block k
 // does not read: one barrier per block, and the loads overlap the arithmetic.
 // Thread (q, x) computes channel quad q of column x with a rotating 3x3 window
 // of LDS reads; 16 lanes cover a token's 128 bytes, so LDS reads and the
-// output stores are contiguous (plain stores: at 1000 views 6% faster than
-// non-temporal ones together with the load policy above, same bits). The
-// grid is a multiple of the channel-block count, so a workgroup's strips share
-// one channel block and it loads its filters once.
+// output stores are contiguous. The grid is a multiple of the channel-block
+// count, so a workgroup's strips share one channel block and it loads its
+// filters once.
 //
 // shortconv_kernel (everything else: fp32, wider grids, other channel counts):
 // a work item is one (view, column x, segment of SEG rows, block of up to 256
@@ -371,7 +369,7 @@ __global__ __launch_bounds__(LDS_NT) void shortconv_lds_kernel(const uint16_t* _
       if (j < row_chunks) {
         const uint16_t* g = src + ((int64_t)row * grid_w + j / NCH) * C + 8 * (j % NCH);
         __builtin_amdgcn_global_load_lds(g, (lds_void*)((lds_u16*)ring + (slot * W2 + 1) * CB + k * 512), 16, 0,
-                                         3);
+                                         0);
       }
       k += NW;
       while (k >= pieces_per_row) {
@@ -431,7 +429,8 @@ __global__ __launch_bounds__(LDS_NT) void shortconv_lds_kernel(const uint16_t* _
               const float p = wt[3 * dy + dx][j] * win[(r + dy) % 3][dx][j];
               acc[j] = acc[j] + p;
             }
-        *reinterpret_cast<u32x2*>(ob + ((int64_t)r * grid_w + x) * C) = ConvTraits<true>::narrow(acc);
+        __builtin_nontemporal_store(ConvTraits<true>::narrow(acc),
+                                    reinterpret_cast<u32x2*>(ob + ((int64_t)r * grid_w + x) * C));
       }
     }
   };
