@@ -22,14 +22,29 @@ constexpr int PER_HEAD = 3 * DM;
 // so the chain G^T = W_g^T Q^T -> H^T -> Y^T = W_d^T H^T contracts over e and
 // then over hidden units with no transposes: each H^T tile is consumed from
 // registers. Weights sit in LDS, pre-permuted to match the operand orders.
-// Each wave handles 32 tokens per iteration.
+//
+// All products use 16x16x32 MFMA tiles. A wave takes 32 tokens per iteration
+// as two 16-token halves that share every weight operand read from LDS (one
+// read feeds two MFMAs). With 16 tokens per MFMA column block, each query
+// load instruction covers 16 token rows x 64 contiguous bytes and each output
+// store 16 rows x 64 bytes, where 32x32 tiles touch 32 rows x 32 bytes: half
+// the cache lines per memory instruction.
 // ---------------------------------------------------------------------------
-constexpr int RT = 32;  // tokens per wave iteration
+constexpr int RT = 32;  // tokens per wave iteration (two 16-token halves)
 constexpr int NW = 8;   // waves per workgroup
 // Two workgroups per CU (four waves per SIMD) need at most 128 VGPRs per lane;
-// the kernel compiles to 128 (check num_vgpr in the assembly after changes).
+// the kernel compiles to 114 without spills (check the resource usage after
+// changes).
 
-__global__ __launch_bounds__(512, 2) void read_bf16_kernel(const uint16_t* __restrict__ Q,
+// 16x16x32 bf16 MFMA, fp32 accumulate.
+//   A operand: lane l holds A[row = l%16][k = 8*(l/16) + j], j = 0..7
+//   B operand: lane l holds B[k = 8*(l/16) + j][col = l%16]
+//   C/D:       lane l, register r holds C[row = 4*(l/16) + r][col = l%16]
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(512, 4) void read_bf16_kernel(const uint16_t* __restrict__ Q,
                                                            const float* __restrict__ theta,
                                                            uint16_t* __restrict__ O, int64_t n_tokens,
                                                            int n_heads, int P, int64_t n_blocks) {
@@ -43,26 +58,27 @@ __global__ __launch_bounds__(512, 2) void read_bf16_kernel(const uint16_t* __res
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so tile offsets stay scalar
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;  // k-quarter of an operand, row quad of a result
   const int64_t C = (int64_t)n_heads * D;
   const float* th = theta + (int64_t)head * PER_HEAD;
 
-  // A operand of G^T for k-step ks: lane (row hid, half hh) supplies
-  // W_g[e = 32hh + 8ks + j][hid]; stored at WgP[hid][16ks + 8hh + j].
+  // A operand of G^T (rows hid, k = e): WgP[hid][e] = W_g[e][hid], and W_u
+  // likewise. The 144-byte row pitch keeps 16 lanes reading 16 rows
+  // conflict-free.
   for (int idx = tid; idx < M * D; idx += 64 * NW) {
-    const int hid = idx / D, kk = idx % D;
-    const int ks = kk >> 4, h2 = (kk >> 3) & 1, j = kk & 7;
-    const int e = 32 * h2 + 8 * ks + j;
-    WgP[hid * KP + kk] = f32_to_bf16_bits(th[e * M + hid]);
-    WuP[hid * KP + kk] = f32_to_bf16_bits(th[DM + e * M + hid]);
+    const int e = idx / M, hid = idx % M;
+    WgP[hid * KP + e] = f32_to_bf16_bits(th[e * M + hid]);
+    WuP[hid * KP + e] = f32_to_bf16_bits(th[DM + e * M + hid]);
   }
-  // A operand of Y^T for k-step s: lane (row o, half hh) supplies
-  // W_d[hid = 16s + 8(j/4) + 4hh + j%4][o] (the register order of H^T).
+  // A operand of Y^T for k-step s (32 hidden units): lane (row o, quarter g)
+  // supplies W_d[hid][o] for hid = 32s + 4g + j (j < 4) and 32s + 16 + 4g +
+  // j - 4 (j >= 4): the order in which a lane holds H^T (rows 4g..4g+3 of the
+  // two 16-row G^T tiles of that k-step).
   for (int idx = tid; idx < D * M; idx += 64 * NW) {
     const int o = idx / M, kk = idx % M;
-    const int s = kk >> 4, h2 = (kk >> 3) & 1, j = kk & 7;
-    const int hid = 16 * s + 8 * (j >> 2) + 4 * h2 + (j & 3);
+    const int s = kk >> 5, gg = (kk >> 3) & 3, j = kk & 7;
+    const int hid = 32 * s + (j < 4 ? 4 * gg + j : 16 + 4 * gg + j - 4);
     WdP[o * HP + kk] = f32_to_bf16_bits(th[2 * DM + hid * D + o]);
   }
   __syncthreads();
@@ -71,89 +87,100 @@ __global__ __launch_bounds__(512, 2) void read_bf16_kernel(const uint16_t* __res
   const int64_t tile_begin = n_tiles * chunk / P;
   const int64_t tile_end = n_tiles * (chunk + 1) / P;
 
-  // Each wave walks tiles tile_begin + w, + NW, ...; the next tile's queries
-  // are loaded while the current one computes. Q and O are accessed through
-  // buffer descriptors built per tile from 64-bit scalar arithmetic, based at
-  // the tile's first token and this head, with a range that ends at the
-  // tensor's end: rows at or past n_tokens read as zeros and their stores are
-  // dropped, so loads and stores are unconditional and the lane offsets fixed.
-  const int lane_off = (l32 * (int)C + 32 * hh) * 2;
+  // Q and O are accessed through buffer descriptors built per tile from
+  // 64-bit scalar arithmetic, based at the tile's first token and this head,
+  // with a range that ends at the tensor's end: rows at or past n_tokens read
+  // as zeros and their stores are dropped, so loads and stores are
+  // unconditional and the lane offsets fixed. Lane (token l16, quarter g)
+  // loads channels 32ks + 8g .. +7 of its token for k-step ks.
+  const int lane_off = (l16 * (int)C + 8 * g) * 2;
   auto tile_res = [&](const uint16_t* base, int64_t tile) {
     const int64_t t0 = tile * RT;
     const int64_t range = (n_tokens - t0) * C * 2 - (int64_t)head * D * 2;
     const int nrec = (int)(range > 0x7fffffffLL ? 0x7fffffffLL : (range > 0 ? range : 0));
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + t0 * C + (int64_t)head * D), (short)0, nrec, 0x00020000);
   };
-  auto load_q = [&](int64_t tile, u32x4 (&dst)[4]) {
-    const __amdgpu_buffer_rsrc_t r = tile_res(Q, tile);
+  auto compute_tile = [&](int64_t tile) {
+    const __amdgpu_buffer_rsrc_t qres = tile_res(Q, tile);
+    bf16x8 q[2][2];  // [half b][k-step ks]
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      dst[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off + 16 * ks, 0, 0));
-  };
-  // Two query register sets alternate (no loop-carried copies, so the load
-  // waits stay exact): tile k computes from one set while tile k+1 loads into
-  // the other.
-  auto compute_tile = [&](int64_t tile, const u32x4 (&qr)[4]) {
-    bf16x8 q[4];
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) q[ks] = as_bf16x8(qr[ks]);
+      for (int ks = 0; ks < 2; ++ks)
+        q[b][ks] = as_bf16x8(__builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(qres, lane_off + 32 * (int)C * b + 64 * ks, 0, 0)));
     // The weight reads below are loop-invariant; an opaque zero offset keeps the
-    // compiler from hoisting 48 operand vectors into registers (and spilling).
+    // compiler from hoisting the operand vectors into registers (and spilling).
     int lds0 = 0;
     asm volatile("" : "+v"(lds0));
-    f32x16 accY[2] = {f32x16{}, f32x16{}};
+    f32x4 accY[2][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x16 g = f32x16{}, u = f32x16{};
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int off = lds0 + (32 * mt + l32) * KP + 16 * ks + 8 * hh;
-        g = mfma32(ld_op(&WgP[off]), q[ks], g);
-        u = mfma32(ld_op(&WuP[off]), q[ks], u);
-      }
-      float h[16];
+      for (int ot = 0; ot < 4; ++ot) accY[b][ot] = f32x4{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float s = sigmoid_fast(g[r]);
-        h[r] = g[r] * s * u[r];
-      }
+    for (int s = 0; s < 4; ++s) {
+      // G^T and U^T rows 32s..32s+15 (tile 0) and 32s+16..32s+31 (tile 1).
+      f32x4 g0[2], g1[2], u0[2], u1[2];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const bf16x8 hop = pack8(&h[8 * half]);
-        const int s = 2 * mt + half;
+      for (int b = 0; b < 2; ++b) g0[b] = g1[b] = u0[b] = u1[b] = f32x4{};
 #pragma unroll
-        for (int ot = 0; ot < 2; ++ot) {
-          accY[ot] = mfma32(ld_op(&WdP[lds0 + (32 * ot + l32) * HP + 16 * s + 8 * hh]), hop, accY[ot]);
+      for (int ks = 0; ks < 2; ++ks) {
+        const int off0 = lds0 + (32 * s + l16) * KP + 32 * ks + 8 * g;
+        const int off1 = off0 + 16 * KP;
+        const bf16x8 ag0 = ld_op(&WgP[off0]), au0 = ld_op(&WuP[off0]);
+        const bf16x8 ag1 = ld_op(&WgP[off1]), au1 = ld_op(&WuP[off1]);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          g0[b] = mfma16(ag0, q[b][ks], g0[b]);
+          u0[b] = mfma16(au0, q[b][ks], u0[b]);
+          g1[b] = mfma16(ag1, q[b][ks], g1[b]);
+          u1[b] = mfma16(au1, q[b][ks], u1[b]);
         }
       }
-    }
-    // Output row o of Y^T tile ot is 8q + 4hh + i (q = r/4, i = r%4) in lane
-    // half hh. Exchanging the q-odd quads of the low half with the q-even
-    // quads of the high half (v_permlane32_swap) gives every lane 8
-    // consecutive outputs, stored as one 16-byte write.
-    const __amdgpu_buffer_rsrc_t ores = tile_res(O, tile);
+      // H^T = silu(G^T) * U^T, packed as the B operand of k-step s.
+      bf16x8 hop[2];
 #pragma unroll
-    for (int ot = 0; ot < 2; ++ot) {
+      for (int b = 0; b < 2; ++b) {
+        float h[8];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const f32x16& a = accY[ot];
-        const uint32_t y0 = pack_bf16x2(a[8 * p + 0], a[8 * p + 1]), y1 = pack_bf16x2(a[8 * p + 2], a[8 * p + 3]);
-        const uint32_t x0 = pack_bf16x2(a[8 * p + 4], a[8 * p + 5]), x1 = pack_bf16x2(a[8 * p + 6], a[8 * p + 7]);
-        const auto s0 = __builtin_amdgcn_permlane32_swap(y0, x0, false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(y1, x1, false, false);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{s0[0], s1[0], s0[1], s1[1]}, ores,
-                                               (l32 * (int)C + 32 * ot + 16 * p + 8 * hh) * 2, 0, 0);
+        for (int r = 0; r < 4; ++r) {
+          h[r] = g0[b][r] * sigmoid_fast(g0[b][r]) * u0[b][r];
+          h[4 + r] = g1[b][r] * sigmoid_fast(g1[b][r]) * u1[b][r];
+        }
+        hop[b] = pack8(h);
+      }
+#pragma unroll
+      for (int ot = 0; ot < 4; ++ot) {
+        const bf16x8 wd = ld_op(&WdP[lds0 + (16 * ot + l16) * HP + 32 * s + 8 * g]);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) accY[b][ot] = mfma16(wd, hop[b], accY[b][ot]);
       }
     }
+    // Lane (token l16, quad g) holds outputs 16ot + 4g .. +3 of Y^T tile ot.
+    // v_permlane16_swap exchanges the odd row groups of tile 2p with the even
+    // row groups of tile 2p+1, after which quad g holds the 8 consecutive
+    // outputs 32p + 16(g&1) + 8(g>>1) .. +7, stored as one 16-byte write.
+    const __amdgpu_buffer_rsrc_t ores = tile_res(O, tile);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const f32x4& x = accY[b][2 * p];
+        const f32x4& y = accY[b][2 * p + 1];
+        const uint32_t xa = pack_bf16x2(x[0], x[1]), xb = pack_bf16x2(x[2], x[3]);
+        const uint32_t ya = pack_bf16x2(y[0], y[1]), yb = pack_bf16x2(y[2], y[3]);
+        const auto sa = __builtin_amdgcn_permlane16_swap(xa, ya, false, false);
+        const auto sb = __builtin_amdgcn_permlane16_swap(xb, yb, false, false);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{sa[0], sb[0], sa[1], sb[1]}, ores,
+            ((16 * b + l16) * (int)C + 32 * p + 16 * (g & 1) + 8 * (g >> 1)) * 2, 0, 0);
+      }
   };
-  u32x4 qa[4], qb[4];
-  load_q(tile_begin + w, qa);
-  for (int64_t tile = tile_begin + w; tile < tile_end; tile += 2 * NW) {
-    load_q(tile + NW, qb);
-    compute_tile(tile, qa);
-    load_q(tile + 2 * NW, qa);
-    if (tile + NW < tile_end) compute_tile(tile + NW, qb);
-  }
+  // Each wave walks tiles tile_begin + w, + NW, ... and loads a tile's
+  // queries just before computing it: the other waves on the SIMD cover the
+  // load latency, and no second query register set is held.
+  for (int64_t tile = tile_begin + w; tile < tile_end; tile += NW) compute_tile(tile);
 }
 
 }  // namespace
