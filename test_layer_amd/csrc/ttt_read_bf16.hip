@@ -63,13 +63,17 @@ __global__ __launch_bounds__(512, 4) void read_bf16_kernel(const uint16_t* __res
   const int64_t C = (int64_t)n_heads * D;
   const float* th = theta + (int64_t)head * PER_HEAD;
 
-  // A operand of G^T (rows hid, k = e): WgP[hid][e] = W_g[e][hid], and W_u
-  // likewise. The 144-byte row pitch keeps 16 lanes reading 16 rows
+  // A operand of G'^T (rows hid, k = e): WgP[hid][e] = -log2(e) W_g[e][hid],
+  // WuP[hid][e] = -ln(2) W_u[e][hid]. The two scales fold the exp2 argument
+  // of the sigmoid into the weights: with G' = -log2(e) G and U' = -ln(2) U,
+  // silu(G) U = G' U' / (1 + 2^G'), since log2(e) ln(2) = 1. That saves one
+  // multiply per hidden unit; each weight is still rounded once to bf16 (after
+  // its scaling). The 144-byte row pitch keeps 16 lanes reading 16 rows
   // conflict-free.
   for (int idx = tid; idx < M * D; idx += 64 * NW) {
     const int e = idx / M, hid = idx % M;
-    WgP[hid * KP + e] = f32_to_bf16_bits(th[e * M + hid]);
-    WuP[hid * KP + e] = f32_to_bf16_bits(th[DM + e * M + hid]);
+    WgP[hid * KP + e] = f32_to_bf16_bits(th[e * M + hid] * -1.4426950408889634f);
+    WuP[hid * KP + e] = f32_to_bf16_bits(th[DM + e * M + hid] * -0.6931471805599453f);
   }
   // A operand of Y^T for k-step s (32 hidden units): lane (row o, quarter g)
   // supplies W_d[hid][o] for hid = 32s + 4g + j (j < 4) and 32s + 16 + 4g +
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(512, 4) void read_bf16_kernel(const uint16_t* __res
       for (int ot = 0; ot < 4; ++ot) accY[b][ot] = f32x4{};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      // G^T and U^T rows 32s..32s+15 (tile 0) and 32s+16..32s+31 (tile 1).
+      // G'^T and U'^T rows 32s..32s+15 (tile 0) and 32s+16..32s+31 (tile 1).
       f32x4 g0[2], g1[2], u0[2], u1[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) g0[b] = g1[b] = u0[b] = u1[b] = f32x4{};
@@ -138,15 +142,16 @@ __global__ __launch_bounds__(512, 4) void read_bf16_kernel(const uint16_t* __res
           u1[b] = mfma16(au1, q[b][ks], u1[b]);
         }
       }
-      // H^T = silu(G^T) * U^T, packed as the B operand of k-step s.
+      // H^T = silu(G^T) * U^T = G'^T U'^T / (1 + 2^G'^T), packed as the B
+      // operand of k-step s.
       bf16x8 hop[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         float h[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          h[r] = g0[b][r] * sigmoid_fast(g0[b][r]) * u0[b][r];
-          h[4 + r] = g1[b][r] * sigmoid_fast(g1[b][r]) * u1[b][r];
+          h[r] = g0[b][r] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g0[b][r])) * u0[b][r];
+          h[4 + r] = g1[b][r] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g1[b][r])) * u1[b][r];
         }
         hop[b] = pack8(h);
       }
