@@ -87,7 +87,10 @@ def _bits_equal(a, b):
 READ_CASES = [
     # (n, heads, d, m, dtype)
     (1, 16, 64, 128, torch.bfloat16),
+    (16, 16, 64, 128, torch.bfloat16),
+    (17, 5, 64, 128, torch.bfloat16),
     (31, 16, 64, 128, torch.bfloat16),
+    (48, 16, 64, 128, torch.bfloat16),
     (997, 16, 64, 128, torch.bfloat16),
     (4122, 3, 64, 128, torch.bfloat16),
     (37, 2, 16, 32, torch.float32),

@@ -125,8 +125,10 @@ def test_shortconv_bf16_extreme_values_bitexact():
 # Read
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("n_tokens", [1, 31, 1000, 4122])
+@pytest.mark.parametrize("n_tokens", [1, 16, 17, 31, 48, 1000, 4122])
 def test_read_bf16_parity(n_tokens):
+    """Token counts around the kernel's 32-token tile and its two 16-token
+    halves (a last tile with an empty, a one-token and a full second half)."""
     cfg = _small_vggt(views=3)
     print(f"[read bf16] n={n_tokens}", flush=True)
     inp = make_inputs(cfg, DEV)
@@ -135,6 +137,16 @@ def test_read_bf16_parity(n_tokens):
     ref = oracle.ttt_read(to64(Q), inp.theta0.cpu().numpy(), cfg.n_heads, cfg.d_head, cfg.d_hidden)
     err = rel_err_per_head(to64(O), ref, cfg.n_heads)
     assert err.max() <= TOL_BF16, err
+    # Per token and head as well, so that one wrong token among thousands
+    # cannot hide in a per-head norm. A screen for gross errors (a token left
+    # at zero, read from the wrong row or with permuted outputs gives about
+    # 1): each token's error relative to the head's mean token norm.
+    d = cfg.d_head
+    o = to64(O).reshape(n_tokens, cfg.n_heads, d)
+    r = ref.reshape(n_tokens, cfg.n_heads, d)
+    tok_err = np.linalg.norm(o - r, axis=2) / np.linalg.norm(r, axis=2).mean(axis=0)
+    print(f"[read bf16] per-token max {tok_err.max():.2e}", flush=True)
+    assert tok_err.max() <= 5 * TOL_BF16, tok_err.max()
 
 
 def test_read_bf16_trained_weights_parity():
