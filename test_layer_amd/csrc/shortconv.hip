@@ -8,22 +8,24 @@
 //
 // Design (HBM-bound stencil). Two kernels share one arithmetic contract.
 //
-// shortconv_lds_kernel (bf16, 3x3, channels a multiple of 64, grid rows up to
-// 126 columns): an LDS-haloed stencil. A workgroup walks strips (view, block of
-// 64 channels) down the grid in blocks of 3 output rows. LDS holds a ring of 10
-// staged input rows [slot][column][64 channels] (bf16, 128 bytes per token)
-// with a zero column on each side; every block brings in the rows it needs that
-// are not staged yet (a strip's first block: the zero row above the grid and
-// rows 0..3; later blocks: the next 3 rows, or the zero row below the grid) with
-// direct global -> LDS loads (global_load_lds_dwordx4, one 64-lane instruction
-// per 1 KB of a row), so each input row is read from HBM once. Those loads for
-// block k + 1 are issued before block k is computed and fill ring slots block k
-// does not read: one barrier per block, and the loads overlap the arithmetic.
-// Thread (q, x) computes channel quad q of column x with a rotating 3x3 window
-// of LDS reads; 16 lanes cover a token's 128 bytes, so LDS reads and the
-// output stores are contiguous. The grid is a multiple of the channel-block
-// count, so a workgroup's strips share one channel block and it loads its
-// filters once.
+// shortconv_lds_kernel<CB, R, NT> (bf16, 3x3, channels a multiple of 64, grid
+// rows up to 126 columns): an LDS-haloed stencil. A workgroup walks strips
+// (view, block of CB channels) down the grid in blocks of R output rows. LDS
+// holds a ring of 2R + 4 staged input rows [slot][column][CB channels] (bf16,
+// 2 CB bytes per token) with a zero column on each side; every block brings in
+// the rows it needs that are not staged yet (a strip's first block: the zero
+// row above the grid and rows 0..R; later blocks: the next R rows, or the zero
+// row below the grid) with direct global -> LDS loads (global_load_lds_dwordx4,
+// one 64-lane instruction per 1 KB of a row), so each input row is read from
+// HBM once. Those loads for block k + 1 are issued before block k is computed
+// and fill ring slots block k does not read: one barrier per block, and the
+// loads overlap the arithmetic. Thread (q, x) computes channel quad q of column
+// x with a rotating 3x3 window of LDS reads; CB / 4 lanes cover a token's
+// 2 CB bytes, so LDS reads and the output stores are contiguous. The grid is a
+// multiple of the channel-block count, so a workgroup's strips share one
+// channel block and it loads its filters once. 128-channel strips (256
+// contiguous bytes per token and access) are used where C allows and the ring
+// fits, 64-channel strips otherwise.
 //
 // shortconv_kernel (everything else: fp32, wider grids, other channel counts):
 // a work item is one (view, column x, segment of SEG rows, block of up to 256
@@ -300,12 +302,18 @@ __global__ __launch_bounds__(256) void shortconv_kxk_kernel(const char* __restri
 
 // ---------------------------------------------------------------------------
 // LDS-haloed form (bf16, 3x3); see the file header.
-constexpr int LDS_CB = 64;         // channels per strip (128 bytes per token)
-constexpr int LDS_R = 3;           // output rows per block
-constexpr int LDS_NS = 2 * LDS_R + 4;  // ring slots
-constexpr int LDS_NT = 256;        // threads per workgroup
-constexpr int LDS_WG_PER_CU = 3;   // 3 x 49.9 KB of LDS at 37 columns
+// Two shapes of the ring, as template parameters <CB channels per strip, R
+// output rows per block, NT threads>:
+//   <128, 2, 512>: 256 bytes per token and strip, 8 slots (79.9 KB at 37
+//     columns), two workgroups per CU; used when C is a multiple of 128 and
+//     the ring fits.
+//   <64, 3, 256>: 128 bytes per token, 10 slots (49.9 KB at 37 columns), three
+//     workgroups per CU; every other bf16 case with C a multiple of 64.
 constexpr size_t LDS_MAX_BYTES = 160 * 1024;
+template <int CB, int R>
+constexpr size_t lds_ring_bytes(int grid_w) {
+  return (size_t)(2 * R + 4) * (grid_w + 2) * CB * 2;
+}
 
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -318,12 +326,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 // at `start` (its first introduced slot for b = 0, two before it otherwise);
 // the next block's rows go to the R + 2 slots after them, which this block does
 // not read. That needs 2R + 4 slots.
-__global__ __launch_bounds__(LDS_NT) void shortconv_lds_kernel(const uint16_t* __restrict__ V,
+template <int CB, int R, int NT>
+__global__ __launch_bounds__(NT) void shortconv_lds_kernel(const uint16_t* __restrict__ V,
                                                               uint16_t* __restrict__ Vp, const float* __restrict__ w,
                                                               int64_t n_strips, int grid_h, int grid_w, int n_special,
                                                               int C, int n_cb, int pieces_per_row) {
   extern __shared__ __attribute__((aligned(16))) uint16_t ring[];
-  constexpr int CB = LDS_CB, R = LDS_R, NS = LDS_NS, NT = LDS_NT;
+  constexpr int NS = 2 * R + 4;  // ring slots
   constexpr int NQ = CB / 4;   // 4-channel quads per token
   constexpr int NCH = CB / 8;  // 16-byte chunks per token
   constexpr int NW = NT / 64;
@@ -460,7 +469,32 @@ __global__ __launch_bounds__(LDS_NT) void shortconv_lds_kernel(const uint16_t* _
   }
 }
 
-size_t lds_ring_bytes(int grid_w) { return (size_t)LDS_NS * (grid_w + 2) * LDS_CB * 2; }
+
+// Launches the LDS ring kernel with a grid that is a multiple of the channel
+// block count, so that the strips s, s + G, ... of a workgroup share a channel
+// block. False (and nothing launched) if the ring needs more dynamic LDS than
+// the device grants.
+template <int CB, int R, int NT>
+bool launch_lds(const void* V, void* Vp, const float* w, int64_t n_views, int grid_h, int grid_w, int n_special,
+                int C, int wg_per_cu, hipStream_t stream) {
+  const size_t ring_bytes = lds_ring_bytes<CB, R>(grid_w);
+  if (ring_bytes > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&shortconv_lds_kernel<CB, R, NT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)ring_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  const int n_cb = C / CB;
+  const int64_t n_strips = n_views * n_cb;
+  int64_t g = (int64_t)wg_per_cu * 256 / n_cb;
+  g = (g < 1 ? 1 : g) * n_cb;
+  if (g > n_strips) g = n_strips;
+  const int pieces_per_row = (grid_w * (CB / 8) + 63) / 64;
+  hipLaunchKernelGGL((shortconv_lds_kernel<CB, R, NT>), dim3((unsigned)g), dim3(NT), ring_bytes, stream,
+                     static_cast<const uint16_t*>(V), static_cast<uint16_t*>(Vp), w, n_strips, grid_h, grid_w,
+                     n_special, C, n_cb, pieces_per_row);
+  return true;
+}
 
 }  // namespace
 
@@ -495,27 +529,12 @@ hipError_t launch_shortconv(const void* V, void* Vp, const float* w, int64_t n_v
   // so the filters are loaded once per workgroup rather than once per item.
   const int64_t max_grid = (int64_t)VGGT3_CONV_WG_PER_CU * 256;
   const unsigned n_blocks = (unsigned)(n_work < max_grid ? n_work : max_grid);
-  const size_t ring_bytes = lds_ring_bytes(grid_w);
-  if (bf16 && C % LDS_CB == 0 && ring_bytes <= LDS_MAX_BYTES) {
-    bool ok = true;
-    if (ring_bytes > 64 * 1024)
-      ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&shortconv_lds_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)ring_bytes) == hipSuccess;
-    if (ok) {
-      const int n_cb = C / LDS_CB;
-      const int64_t n_strips = n_views * n_cb;
-      // a multiple of n_cb, so that the strips s, s + G, ... of a workgroup share a channel block
-      int64_t g = (int64_t)LDS_WG_PER_CU * 256 / n_cb;
-      g = (g < 1 ? 1 : g) * n_cb;
-      if (g > n_strips) g = n_strips;
-      const int pieces_per_row = (grid_w * (LDS_CB / 8) + 63) / 64;
-      hipLaunchKernelGGL(shortconv_lds_kernel, dim3((unsigned)g), dim3(LDS_NT), ring_bytes, stream,
-                         static_cast<const uint16_t*>(V), static_cast<uint16_t*>(Vp), w, n_strips, grid_h, grid_w,
-                         n_special, C, n_cb, pieces_per_row);
-      return hipGetLastError();
-    }
-    (void)hipGetLastError();
-  }
+  if (bf16 && C % 128 == 0 && lds_ring_bytes<128, 2>(grid_w) <= LDS_MAX_BYTES &&
+      launch_lds<128, 2, 512>(V, Vp, w, n_views, grid_h, grid_w, n_special, C, 2, stream))
+    return hipGetLastError();
+  if (bf16 && C % 64 == 0 && lds_ring_bytes<64, 3>(grid_w) <= LDS_MAX_BYTES &&
+      launch_lds<64, 3, 256>(V, Vp, w, n_views, grid_h, grid_w, n_special, C, 3, stream))
+    return hipGetLastError();
   if (bf16)
     hipLaunchKernelGGL(shortconv_kernel<true>, dim3(n_blocks), dim3(256), 0, stream, static_cast<const char*>(V),
                        static_cast<char*>(Vp), w, n_work, grid_h, grid_w, n_special, C, n_seg, n_cblk);
