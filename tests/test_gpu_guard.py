@@ -160,8 +160,9 @@ def test_gradient_reads_only_its_rows(case, loss):
 
 CONV_CASES = [
     # (views, grid_h, grid_w, n_special, C, ksize, dtype)
-    (2, 37, 37, 5, 1024, 3, torch.bfloat16),  # LDS ring kernel
+    (2, 37, 37, 5, 1024, 3, torch.bfloat16),  # LDS ring kernel, 128-channel strips
     (3, 5, 7, 2, 128, 3, torch.bfloat16),
+    (2, 7, 40, 3, 192, 3, torch.bfloat16),    # LDS ring kernel, 64-channel strips
     (1, 4, 127, 1, 64, 3, torch.bfloat16),    # register-window kernel
     (2, 8, 8, 0, 16, 3, torch.float32),
     (2, 9, 11, 3, 64, 5, torch.bfloat16),     # V-5

@@ -63,11 +63,19 @@ CONV_CASES = [
     (1, 1, 1, 1, 1, 8, "bf16"),
     (4, 3, 2, 0, 2, 4, "f32"),
     (2, 37, 37, 5, 4, 64, "f32"),
-    # bf16, 64-channel multiples, rows up to 126 columns: the LDS ring kernel
+    # bf16, 64-channel multiples, rows up to 126 columns: the LDS ring kernel,
+    # 64-channel strips of 3-row blocks
     (2, 9, 126, 1, 1, 64, "bf16"),  # widest grid row that fits LDS (160 KB)
     (2, 7, 40, 3, 3, 64, "bf16"),   # three channel blocks
     (5, 4, 4, 2, 1, 64, "bf16"),    # a ragged last block of rows
     (3, 1, 9, 0, 1, 64, "bf16"),    # a single grid row
+    (2, 9, 79, 1, 2, 64, "bf16"),   # C = 128, but the 128-channel ring would exceed 160 KB
+    # with C a multiple of 128 (and rows up to 78 columns): 128-channel strips
+    # of 2-row blocks
+    (2, 9, 78, 1, 2, 64, "bf16"),   # widest grid row for that ring (160 KB)
+    (5, 5, 4, 2, 2, 64, "bf16"),    # a ragged last block of rows
+    (3, 1, 9, 0, 2, 64, "bf16"),    # a single grid row
+    (2, 2, 3, 0, 4, 64, "bf16"),    # two channel blocks, a tiny grid
     # bf16 outside it: the register-window kernel
     (1, 4, 127, 0, 1, 64, "bf16"),  # grid row too wide for the LDS ring
     (1, 2, 3, 0, 3, 32, "bf16"),    # 96 channels
