@@ -31,11 +31,6 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 SPEC_CLOCK_GHZ = 2.4
-# Shader clock under the gradient kernel, from the committed counter run
-# (profiles/ttt_layer_views1000_counters.md): its GPU-active cycles, converted
-# at the 2.4 GHz spec clock (2.815 ms), against the event-timed launch of the
-# same profiled run (3.762 ms).
-COUNTER_CLOCK_GHZ = round(SPEC_CLOCK_GHZ * 2.815 / 3.762, 2)
 PEAK_HBM_GBS = 8000.0
 METRIC = "TTT-layer tokens/sec (write+read) at 1000 views; % bf16 MFMA peak"
 # The gradient kernel each recipe's timed write steps launch (no loss value).
@@ -65,10 +60,12 @@ def source_sha256(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic(recipe="mse_gd", config="views1000"):
-    """HBM bytes per launch of the gradient kernel from the committed rocprofv3
-    counter summary of this recipe and workload, or None if there is none or it
-    was taken on different kernel source."""
+def load_counter_record(recipe, config, kernel):
+    """The committed rocprofv3 counter record of the gradient kernel for this
+    recipe and workload (HBM bytes per launch, and the shader clock the kernel
+    ran at: its GPU-active cycles over its event-timed launch on the profiled
+    box), or None if there is none, it covers another kernel, or it was taken
+    on different kernel source."""
     tag = config if recipe == "mse_gd" else f"{recipe}_{config}"
     path = TRAFFIC_FILE.replace("_views1000", f"_{tag}")
     try:
@@ -76,9 +73,9 @@ def load_traffic(recipe="mse_gd", config="views1000"):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != source_sha256(GRAD_SOURCE):
+    if rec.get("kernel") != kernel or rec.get("source_sha256") != source_sha256(GRAD_SOURCE):
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec
 
 
 def cpu_baseline(inp, cfg, target_s=15.0, max_views=256, loss="mse", opt="gd"):
@@ -322,8 +319,8 @@ def wide_bench(args, loss_kind, opt_kind, recipe_desc):
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
-            "clock_GHz_from_counters": COUNTER_CLOCK_GHZ,
-            "frac_at_counter_clock": achieved / (PEAK_BF16_TFLOPS * COUNTER_CLOCK_GHZ / SPEC_CLOCK_GHZ),
+            "clock_GHz_from_counters": None,
+            "frac_at_counter_clock": None,
             "traffic": None,
             "avg_launch_ms": write_ms / cfg.steps,
             "flops_per_launch": fw * n,
@@ -477,6 +474,10 @@ def main():
     fw, fr = flops_per_token(cfg, loss_kind)
     grad_flops = fw * n  # per launch of the gradient kernel
     achieved = grad_flops / (grad_avg_ms * 1e-3) / 1e12
+    grad_kernel = (("grad_partial_bf16_kernel" + ("<dot>" if loss_kind == "dot" else "") + " (with loss value)")
+                   if args.with_loss else GRAD_KERNEL[loss_kind])
+    counter_rec = load_counter_record(args.recipe, cfg.name, grad_kernel)
+    clock = counter_rec.get("clock_GHz") if counter_rec else None
     mlp_frac = (fw * n * cfg.steps + fr * nq) / ((write_ms + read_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
     esz = 2 if cfg.dtype == "bf16" else 4
     conv_bytes = 2 * n * H * d * esz * (2 if args.conv_variant == "kv3" else 1)
@@ -515,15 +516,14 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": (("grad_partial_bf16_kernel" + ("<dot>" if loss_kind == "dot" else "") + " (with loss value)")
-                       if args.with_loss else GRAD_KERNEL[loss_kind]),
+            "kernel": grad_kernel,
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
-            "clock_GHz_from_counters": COUNTER_CLOCK_GHZ,
-            "frac_at_counter_clock": achieved / (PEAK_BF16_TFLOPS * COUNTER_CLOCK_GHZ / SPEC_CLOCK_GHZ),
-            "traffic": load_traffic(args.recipe, cfg.name),
+            "clock_GHz_from_counters": clock,
+            "frac_at_counter_clock": achieved / (PEAK_BF16_TFLOPS * clock / SPEC_CLOCK_GHZ) if clock else None,
+            "traffic": counter_rec["traffic_bytes_per_launch"] if counter_rec else None,
             "avg_launch_ms": grad_avg_ms,
             "flops_per_launch": grad_flops,
         },
