@@ -78,10 +78,12 @@ def load_counter_record(recipe, config, kernel):
     return rec
 
 
-def cpu_baseline(inp, cfg, target_s=15.0, max_views=256, loss="mse", opt="gd"):
+def cpu_baseline(inp, cfg, target_s=15.0, max_views=256, loss="mse", opt="gd", views_fixed=0):
     """The fp64 CPU oracle, as it stands, on the first s views of the same
     scene (conv, `steps` write steps over those tokens, read). s doubles from
-    2 views until one run takes >= target_s / 2 (or max_views)."""
+    2 views until one run takes >= target_s / 2 (or max_views); with
+    views_fixed, s is that many views (all of them for the whole scene), run
+    once."""
     import numpy as np
     import torch
 
@@ -96,9 +98,11 @@ def cpu_baseline(inp, cfg, target_s=15.0, max_views=256, loss="mse", opt="gd"):
     tpv = cfg.tokens_per_view
     w = inp.conv_w.cpu().numpy()
     th0 = inp.theta0.cpu().numpy()
-    views = 2
+    views = min(views_fixed, cfg.n_views) if views_fixed > 0 else 2
     while True:
         n = views * tpv
+        if views_fixed > 0:
+            print(f"[cpu baseline] oracle on the first {views} views ({n} tokens)", file=sys.stderr, flush=True)
         K = inp.K[:n].to(torch.float32).cpu().numpy().astype(np.float64)
         V = inp.V[:n].to(torch.float32).cpu().numpy()
         Q = inp.Q[:n].to(torch.float32).cpu().numpy().astype(np.float64)
@@ -108,7 +112,7 @@ def cpu_baseline(inp, cfg, target_s=15.0, max_views=256, loss="mse", opt="gd"):
                                     cfg.lr, cfg.steps, loss=loss, opt=opt)
         oracle.ttt_read(Q, th, cfg.n_heads, cfg.d_head, cfg.d_hidden)
         dt = time.perf_counter() - t0
-        if dt >= target_s / 2 or views >= max_views or views * 2 > cfg.n_views:
+        if views_fixed > 0 or dt >= target_s / 2 or views >= max_views or views * 2 > cfg.n_views:
             break
         views *= 2
     return {
@@ -334,7 +338,8 @@ def wide_bench(args, loss_kind, opt_kind, recipe_desc):
     if args.offload > 0:
         res["offload"] = offload_bench(tla, inp, Vp, cfg, args, loss_kind, opt_kind)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, cfg, loss=loss_kind, opt=opt_kind)
+        res["cpu_baseline"] = cpu_baseline(inp, cfg, loss=loss_kind, opt=opt_kind,
+                                           views_fixed=args.cpu_baseline_views)
     print(json.dumps(res), flush=True)
 
 
@@ -352,6 +357,10 @@ def main():
                     help="fast-weight MLP: 16 per-head SwiGLUs 64 -> 128 -> 64 (default) or the pages' full-width "
                          "1024 -> 4096 -> 1024 SwiGLU")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-views", type=int, default=0, metavar="S",
+                    help="run the CPU oracle baseline once on the first S views (the whole scene if S >= its "
+                         "views) instead of the bounded sample of 10-30 s; 1000 views take about 100 s and "
+                         "about 60 GB of host memory")
     ap.add_argument("--with-loss", action="store_true",
                     help="compute the inner-loss value in every timed write step (as vggt3_ttt_write with a "
                          "loss_out does); by default it is computed once, after timing")
@@ -546,7 +555,8 @@ def main():
         res["conv_fused"] = conv_fused_bench(tla, inp, cfg, args, loss_kind, opt_kind, ws, O)
         res["conv_fused"]["split_conv_and_write_ms"] = conv_ms + write_ms
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, cfg, loss=loss_kind, opt=opt_kind)
+        res["cpu_baseline"] = cpu_baseline(inp, cfg, loss=loss_kind, opt=opt_kind,
+                                           views_fixed=args.cpu_baseline_views)
     print(json.dumps(res), flush=True)
 
 
