@@ -10,9 +10,12 @@
 // and for a taller matrix (W_d) the same map on X^T, written without the
 // transposes as A = X^T X, X = a X + X B. All in fp32, as the per-head Muon.
 //
-// The products are fp32 SIMT GEMMs: 64 x 64 output tiles, 256 threads with a
-// 4 x 4 block each, k slices of 16 staged through LDS. A GEMM's epilogue is
-// out = alpha * acc + beta * E (E elementwise, same shape as out).
+// The products are fp32 GEMMs on the matrix cores (v_mfma_f32_32x32x2_f32,
+// twice the vector FMA rate): 64 x 64 output tiles, 4 waves with a 32 x 32
+// sub-tile each, k slices of 16 staged through LDS. Each output takes its k
+// terms in ascending order, as a sequential fused multiply-add loop would. A
+// GEMM's epilogue is out = alpha * acc + beta * E (E elementwise, same shape as
+// out).
 #include "bf16_ops.hpp"
 #include "kernels.hpp"
 #include "wide.hpp"
@@ -36,10 +39,11 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(const float* __restrict__ 
   __shared__ float As[GK][GT + 4];
   __shared__ float Bs[GK][GT + 4];
   const int t = threadIdx.x;
-  const int tx = t & 15, ty = t >> 4;
+  const int lane = t & 63, w = t >> 6;
+  const int wm = w >> 1, wn = w & 1;  // this wave's 32 x 32 sub-tile
   const int tiles_n = N / GT;
   const int i0 = (blockIdx.x / tiles_n) * GT, j0 = (blockIdx.x % tiles_n) * GT;
-  float acc[4][4] = {};
+  f32x16 acc = {};
   for (int k0 = 0; k0 < K; k0 += GK) {
     if (TA) {  // A(i, k) = A[k * lda + i]: 16 k rows of 64 i
       const int k = t >> 4, i = (t & 15) * 4;
@@ -62,29 +66,26 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(const float* __restrict__ 
       *(f32x4*)&Bs[k][j] = v;
     }
     __syncthreads();
+    // fp32 MFMA 32x32x2: lane l supplies A(32 wm + l % 32, k + l / 32) and
+    // B(k + l / 32, 32 wn + l % 32)
 #pragma unroll
-    for (int k = 0; k < GK; ++k) {
-      const f32x4 a = *(const f32x4*)&As[k][ty * 4];
-      const f32x4 b = *(const f32x4*)&Bs[k][tx * 4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[p][q] = fmaf(a[p], b[q], acc[p][q]);
+    for (int k = 0; k < GK; k += 2) {
+      const float a = As[k + (lane >> 5)][32 * wm + (lane & 31)];
+      const float b = Bs[k + (lane >> 5)][32 * wn + (lane & 31)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
     }
     __syncthreads();
   }
+  // C layout: lane l, register r holds row 8 (r / 4) + 4 (l / 32) + r % 4,
+  // column l % 32 of the wave's 32 x 32 sub-tile.
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int64_t o = (int64_t)(i0 + ty * 4 + p) * N + j0 + tx * 4;
-    f32x4 v;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = alpha * acc[p][q];
-    if (E != nullptr) {
-      const f32x4 e = *(const f32x4*)(E + o);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = fmaf(beta, e[q], v[q]);
-    }
-    *(f32x4*)(C + o) = v;
+  for (int r = 0; r < 16; ++r) {
+    const int i = i0 + 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    const int j = j0 + 32 * wn + (lane & 31);
+    const int64_t o = (int64_t)i * N + j;
+    float v = alpha * acc[r];
+    if (E != nullptr) v = fmaf(beta, E[o], v);
+    C[o] = v;
   }
 }
 
